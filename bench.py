@@ -1,0 +1,227 @@
+"""Benchmark of the routed MoE FFN layer on one MI355X.
+
+A step is one pass of the whole layer (router, top-k, permutation, expert
+SwiGLU with in-register dequant, shared expert, combine) for one decode token
+through a 512-expert top-10 + 1 shared layer (H 2048, I 768, 4-bit group-32
+weights, bf16 activations), with the inputs resident in HBM.  Consecutive
+steps rotate over 16 distinct copies of the layer's weights (21.8 GB) so the
+experts stream from HBM and not from the 256 MB last-level cache.
+
+Prints one JSON line (rank 0, N = 1):
+  value        decode tokens/s (whole job)
+  roofline     HBM roofline of the dominant kernel (expert gate/up + SwiGLU),
+               algorithmic bytes per launch / HIP-event time per launch
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+plus extra fields: expert-weight GB/s of the whole layer, prefill tokens/s.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--copies", type=int, default=16)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 4096-token prefill figure")
+    ap.add_argument("--prefill-steps", type=int, default=16)
+    ap.add_argument("--kernel-reps", type=int, default=2000)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from sparse_moe_router_amd import api, workload
+    from synth import torch_io
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    api.lib()
+
+    spec = synth.SPECS["decode"]
+    E, K, H, I = spec.n_experts, spec.top_k, spec.hidden, spec.inter
+    t0 = time.time()
+    ld0 = synth.gen_layer(spec, seed=0, layer=0)
+    log(f"generated the 512-expert layer in {time.time() - t0:.1f}s")
+    kw0 = torch_io.layer_kwargs(ld0, dev)
+
+    # copies 1..C-1: the same expert bytes at other addresses (experts rotated),
+    # each with its own router and Zipf bias ranking
+    layers = [api.Layer(**kw0)]
+    for c in range(1, args.copies):
+        w, b = synth.gen_router(spec, seed=0, layer=c)
+        routed = {k: tuple(None if t is None else torch.roll(t, shifts=37 * c, dims=0).contiguous() for t in v)
+                  for k, v in kw0["routed"].items()}
+        shared = {k: tuple(None if t is None else t.clone() for t in v) for k, v in kw0["shared"].items()}
+        kw = dict(kw0, router_w=torch.from_numpy(w).to(dev), router_b=torch.from_numpy(b).to(dev),
+                  routed=routed, shared=shared)
+        layers.append(api.Layer(**kw))
+    torch.cuda.synchronize()
+    log(f"{args.copies} weight copies resident ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+
+    n_tok = 256
+    xs = torch_io.x_tensor(synth.gen_x(spec, seed=0, tokens=n_tok).storage, spec.act, dev)
+    ws = api.workspace(layers[0], 4096, dev)
+    y = torch.empty((4096, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        api.moe_layer_forward(layers[i % args.copies], xs[i % n_tok:i % n_tok + 1], 1, y, ws=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / args.steps
+    tok_s = args.steps / (ms / 1e3)
+    log(f"decode: {ms_per_step * 1e3:.2f} us/step, {tok_s:.0f} tok/s")
+
+    # routing of each copy for its first timed token: distinct experts per step
+    ids = torch.empty((1, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((1, K), dtype=torch.float32, device=dev)
+    offs = [torch.empty(E + 1, dtype=torch.int32, device=dev) for _ in range(args.copies)]
+    sps = [torch.empty(K, dtype=torch.int32, device=dev) for _ in range(args.copies)]
+    pp = torch.empty(K, dtype=torch.int32, device=dev)
+    distinct = []
+    for c in range(args.copies):
+        api.moe_router_topk(layers[c], xs[c:c + 1], 1, ids, wts, ws=ws)
+        api.moe_permute(layers[c], ids, 1, offs[c], sps[c], pp, ws)
+        distinct.append(len(set(ids.cpu().numpy().reshape(-1).tolist())))
+    u_mean = float(np.mean(distinct))
+
+    # dominant kernel: expert gate/up + SwiGLU (one kernel per call), timed
+    # with HIP events on the stream it runs on, launches back to back
+    h = torch.empty((K, I), dtype=torch.bfloat16, device=dev)
+    hs = torch.empty((1, I), dtype=torch.bfloat16, device=dev)
+    for r in range(50):
+        c = r % args.copies
+        api.moe_expert_gate_up_q(layers[c], xs[c:c + 1], 1, offs[c], sps[c], h, hs, stream=stream)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for r in range(args.kernel_reps):
+        c = r % args.copies
+        api.moe_expert_gate_up_q(layers[c], xs[c:c + 1], 1, offs[c], sps[c], h, hs, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    k_us = start.elapsed_time(end) * 1e3 / args.kernel_reps
+    gu_bytes_unit = 2 * workload.matrix_bytes(spec.qfmt, I, H)       # gate + up of one expert
+    gu_bytes = (u_mean + 1) * gu_bytes_unit + (u_mean + 1) * H * 2 + (K + 1) * I * 2  # + x reads, h writes
+    achieved = gu_bytes / (k_us * 1e-6) / 1e9
+    log(f"gate/up kernel: {k_us:.2f} us/launch, {achieved:.0f} GB/s")
+
+    exp_bytes = workload.expert_weight_bytes(spec.qfmt, H, I, int(round(u_mean)), spec.n_shared)
+    layer_bytes = workload.spec_layer_bytes(spec, int(round(u_mean)), tokens=1)
+    extra = {
+        "expert_weight_GBps": exp_bytes / (ms_per_step * 1e-3) / 1e9,
+        "expert_weight_frac_of_8TBps": exp_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "layer_algorithmic_GBps": layer_bytes / (ms_per_step * 1e-3) / 1e9,
+        "layer_algorithmic_bytes": layer_bytes,
+        "distinct_experts_per_token": u_mean,
+        "weight_copies": args.copies,
+    }
+
+    if not args.no_prefill:
+        ps = synth.SPECS["prefill"]
+        xp = torch_io.x_tensor(synth.gen_x(ps, seed=0).storage, ps.act, dev)
+        for i in range(2):
+            api.moe_layer_forward(layers[i % args.copies], xp, ps.tokens, y, ws=ws, stream=stream)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.prefill_steps):
+            api.moe_layer_forward(layers[i % args.copies], xp, ps.tokens, y, ws=ws, stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        pms = start.elapsed_time(end) / args.prefill_steps
+        flops = workload.layer_flops(H, I, E, K, ps.tokens, ps.n_shared)
+        extra["prefill_tok_s"] = ps.tokens / (pms * 1e-3)
+        extra["prefill_ms_per_layer"] = pms
+        extra["prefill_TFLOPs"] = flops / (pms * 1e-3) / 1e12
+        extra["prefill_frac_of_bf16_mfma"] = flops / (pms * 1e-3) / 2.5e15
+        log(f"prefill: {pms:.3f} ms/layer, {extra['prefill_tok_s']:.0f} tok/s")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(spec, ld0)
+
+    out = {
+        "metric": "MoE-layer decode tok/s + expert-weight HBM GB/s (% peak); prefill tok/s",
+        "value": tok_s,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode: 1 token/step through one routed MoE FFN layer, hidden 2048, 512 experts, "
+                        "top-10 + 1 shared, intermediate 768, 4-bit sym group-32 fp16-scale weights, bf16 activations, "
+                        "fp32 router with Zipf(1.1) bias; 16 rotating weight copies",
+            "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "expert gate/up + SwiGLU (k_gateup)",
+            "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+            "traffic": None, "us_per_launch": k_us, "algorithmic_bytes_per_launch": gu_bytes,
+        },
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(spec, ld):
+    """The oracle (float64 NumPy) on decode tokens of the same layer, for about 15 s."""
+    import synth
+    from oracle import moe_oracle as mo
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    x = synth.gen_x(spec, seed=0, tokens=64).values
+    t0 = time.time()
+    n = 0
+    while n < 64 and (time.time() - t0 < 15.0 or n < 2):
+        mo.layer_forward(ld, x[n:n + 1], keep_expert_out=False)
+        n += 1
+    dt = time.time() - t0
+    log(f"cpu oracle: {n} tokens in {dt:.1f}s")
+    return {"value": n / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} decode tokens (T=1 each) through the same 512-expert 4-bit layer, float64 NumPy"}
+
+
+if __name__ == "__main__":
+    main()

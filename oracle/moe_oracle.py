@@ -181,35 +181,34 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(xrows, wg, wu, wd, act):
-    """o = W_d round_act(silu(W_g x) * (W_u x)) for each row of ``xrows`` [n][H]."""
+def expert_ffn(xrows, wg, wu, wd, act, h=None):
+    """o = W_d round_act(silu(W_g x) * (W_u x)) for each row of ``xrows`` [n][H].
+
+    Returns (o, h, v) with v the value of silu(g) * u before rounding.  If ``h``
+    is given it replaces the rounded intermediate (teacher forcing at the
+    rounding point); v is still computed.
+    """
     g = np.asarray(xrows, np.float64) @ wg.T
     u = np.asarray(xrows, np.float64) @ wu.T
-    h = round_act(silu(g) * u, act)
-    return h @ wd.T, h
+    v = silu(g) * u
+    if h is None:
+        h = round_act(v, act)
+    return np.asarray(h, np.float64) @ wd.T, np.asarray(h, np.float64), v
 
 
 # ----------------------------------------------------------------------------
 # the layer
 
-class DequantCache:
-    """Dequantised float64 weights of the experts of one ExpertSet, by position."""
-
-    def __init__(self, es, qfmt):
-        self.es, self.qfmt, self._d = es, qfmt, {}
-        self.pos = {int(e): j for j, e in enumerate(es.index)} if len(es.index) else None
-
-    def __call__(self, e):
-        j = self.pos[int(e)] if self.pos is not None else int(e)
-        if j not in self._d:
-            es = self.es
-            self._d[j] = tuple(
-                dequant(m.codes[j], m.scales[j], None if m.mins is None else m.mins[j], self.qfmt)
-                for m in (es.gate, es.up, es.down))
-        return self._d[j]
+def expert_weights(es, e, qfmt):
+    """Dequantised (gate, up, down) of expert id ``e`` of an ExpertSet (by id if the set is indexed)."""
+    j = int(e)
+    if len(es.index):
+        j = int(np.nonzero(es.index == e)[0][0])
+    return tuple(dequant(m.codes[j], m.scales[j], None if m.mins is None else m.mins[j], qfmt)
+                 for m in (es.gate, es.up, es.down))
 
 
-def layer_forward(layer, x, ids=None, keep_expert_out=True):
+def layer_forward(layer, x, ids=None, keep_expert_out=True, h=None, shared_h=None):
     """The routed MoE FFN layer on the exact activations ``x`` [T][H].
 
     ``layer`` is a synth.LayerData (router, routed experts -- all, or a subset
@@ -217,9 +216,13 @@ def layer_forward(layer, x, ids=None, keep_expert_out=True):
     overrides the selection for the downstream steps; logits and weights are
     still computed from the oracle's logits at those ids.
 
+    ``h`` ([T*K][I], sorted order) and ``shared_h`` ([T][I]) replace the
+    rounded intermediate activations of the routed and shared experts if given.
+
     Returns a dict with logits, ids, w, offsets, sorted_pairs, pair_pos,
-    expert_out (o rows in sorted order), h (sorted order), shared_out,
-    shared_h and y, all float64 / int64.
+    expert_out (o rows in sorted order), h and h_pre (sorted order, after and
+    before rounding), shared_out, shared_h, shared_h_pre and y, all float64 /
+    int64.
     """
     spec = layer.spec
     act, k, e_n = spec.act, spec.top_k, spec.n_experts
@@ -230,35 +233,37 @@ def layer_forward(layer, x, ids=None, keep_expert_out=True):
     w = topk_weights(logits, sel)
     offsets, sorted_pairs, pair_pos = permute(sel, e_n)
 
-    deq = DequantCache(layer.routed, spec.qfmt)
     o = np.zeros((t_n * k, hdim)) if keep_expert_out else None
     hs = np.zeros((t_n * k, spec.inter)) if keep_expert_out else None
+    hv = np.zeros((t_n * k, spec.inter)) if keep_expert_out else None
     o_by_pair = np.zeros((t_n * k, hdim))
     for e in range(e_n):
         lo, hi = offsets[e], offsets[e + 1]
         if lo == hi:
             continue
         pairs = sorted_pairs[lo:hi]
-        wg, wu, wd = deq(e)
-        oe, he = expert_ffn(x[pairs // k], wg, wu, wd, act)
+        wg, wu, wd = expert_weights(layer.routed, e, spec.qfmt)
+        oe, he, ve = expert_ffn(x[pairs // k], wg, wu, wd, act, None if h is None else h[lo:hi])
         o_by_pair[pairs] = oe
         if keep_expert_out:
             o[lo:hi] = oe
             hs[lo:hi] = he
+            hv[lo:hi] = ve
 
     shared_out = np.zeros((t_n, hdim))
-    shared_h = []
-    sdeq = DequantCache(layer.shared, spec.qfmt)
+    sh, shv = [], []
     for j in range(layer.shared.n):
-        wg, wu, wd = sdeq(int(layer.shared.index[j]) if len(layer.shared.index) else j)
-        sj, hj = expert_ffn(x, wg, wu, wd, act)
+        wg, wu, wd = expert_weights(layer.shared, layer.shared.index[j] if len(layer.shared.index) else j,
+                                    spec.qfmt)
+        sj, hj, vj = expert_ffn(x, wg, wu, wd, act, None if shared_h is None else shared_h)
         shared_out = shared_out + sj
-        shared_h.append(hj)
+        sh.append(hj)
+        shv.append(vj)
 
     y = combine(shared_out, o_by_pair.reshape(t_n, k, hdim), w)
     return dict(logits=logits, ids=sel, w=w, offsets=offsets, sorted_pairs=sorted_pairs,
-                pair_pos=pair_pos, expert_out=o, h=hs, shared_out=shared_out,
-                shared_h=shared_h, y=y)
+                pair_pos=pair_pos, expert_out=o, h=hs, h_pre=hv, shared_out=shared_out,
+                shared_h=sh, shared_h_pre=shv, y=y)
 
 
 def combine(shared_out, o_tk, w):

@@ -1,0 +1,80 @@
+// Internal launch interface between the C ABI (moe_abi.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kGroup = 32;
+
+struct QMat {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* mins;
+};
+
+inline QMat qmat(const moe_qmat& m) { return QMat{m.codes, m.scales, m.mins}; }
+
+// ---------------------------------------------------------------- router
+struct RouterArgs {
+  const void* x;        // [T][H] act
+  const float* w;       // [E][H]
+  const float* b;       // [E] or null
+  float* logits;        // [T][E]
+  int32_t* ids;         // [T][K]
+  float* wts;           // [T][K]
+  int T, H, E, K, act;
+};
+hipError_t launch_router_logits(const RouterArgs& a, hipStream_t s);
+hipError_t launch_topk(const RouterArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- permutation
+struct PermuteArgs {
+  const int32_t* ids;   // [T*K]
+  int32_t* offsets;     // [E+1]
+  int32_t* sorted_pairs;
+  int32_t* pair_pos;
+  int32_t* chunk_base;  // [n_chunks][E] scratch
+  int T, K, E;
+};
+size_t permute_scratch_ints(int T, int K, int E);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- expert FFN
+struct FfnArgs {
+  QMat gate, up, down;     // routed, expert 0 base
+  QMat sgate, sup, sdown;  // shared expert (n_shared == 1) or unused
+  int n_shared;
+  int T, H, I, E, K, qfmt, act;
+  const void* x;               // [T][H] act
+  const int32_t* offsets;      // [E+1]
+  const int32_t* sorted_pairs; // [T*K]
+  void* h;                     // [T*K][I] act, sorted order
+  void* hs;                    // [T][I] act, shared
+  float* o;                    // [T*K][H] fp32, sorted order
+  float* so;                   // [T][H] fp32, shared (null: shared expert skipped)
+};
+hipError_t launch_gateup(const FfnArgs& a, hipStream_t s);
+hipError_t launch_down(const FfnArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- combine
+struct CombineArgs {
+  const float* o;          // [T*K][H] sorted order
+  const float* so;         // [T][H] or null
+  const int32_t* pair_pos; // [T*K]
+  const float* w;          // [T*K]
+  const void* x_resid;     // [T][H] act or null
+  void* x_next;            // [T][H] act or null
+  float* y;                // [T][H]
+  int T, H, K, act;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- test hook
+hipError_t launch_dequant(const QMat& m, int qfmt, int rows, int cols, float* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,187 @@
+// Token -> expert permutation: a stable counting sort of the (token, slot)
+// pairs by expert id, so that every expert's tokens are contiguous and each
+// expert's weights are streamed once per layer (per-expert dispatch: page 3
+// "The 'Doorbell' Mechanism").
+//
+// Stability (pairs of one expert in increasing pair index) comes from ranking
+// each pair among the lanes of its wave with the same expert (ballots over the
+// id bits) and walking a chunk of pairs in order with one wave.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kChunk = 1024;          // pairs per chunk in the multi-block path
+constexpr int kSmallMaxPairs = 4096;  // single-wave path up to this many pairs
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
+
+// Mask of the valid lanes of this wave holding the same id as this lane.
+__device__ __forceinline__ uint64_t match_same(int e, bool valid, int nbits) {
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bal = __ballot(valid && bit);
+    same &= bit ? bal : ~bal;
+  }
+  return same;
+}
+
+__device__ __forceinline__ int id_bits(int E) {
+  int nb = 0;
+  while ((1 << nb) < E) ++nb;
+  return nb;
+}
+
+// One wave scatters pairs [p0, p1) in order; running[e] holds the next free
+// sorted position of expert e (LDS, owned by this wave).
+__device__ void scatter_chunk(const PermuteArgs& a, int* running, int p0, int p1, int lane, int nbits) {
+  for (int base = p0; base < p1; base += 64) {
+    const int p = base + lane;
+    const bool valid = p < p1;
+    const int e = valid ? a.ids[p] : 0;
+    const uint64_t same = match_same(e, valid, nbits);
+    const int rank = __popcll(same & lanemask_lt(lane));
+    const int cnt = __popcll(same);
+    int pos = 0;
+    if (valid) pos = running[e] + rank;
+    __syncthreads();
+    if (valid) {
+      a.sorted_pairs[pos] = p;
+      a.pair_pos[p] = pos;
+      if (rank == 0) running[e] += cnt;
+    }
+    __syncthreads();
+  }
+}
+
+// Exclusive scan of v over one wave; returns the prefix, total in *tot.
+__device__ __forceinline__ int wave_excl_scan(int v, int lane, int* tot) {
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += n;
+  }
+  *tot = __shfl(incl, 63, 64);
+  return incl - v;
+}
+
+// Small path: one wave does histogram, scan and scatter.
+__global__ __launch_bounds__(64) void k_perm_small(PermuteArgs a) {
+  extern __shared__ int lds[];
+  int* cnt = lds;  // [E]: counts, then running positions
+  const int lane = threadIdx.x;
+  const int n = a.T * a.K, E = a.E;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  __syncthreads();
+  for (int p = lane; p < n; p += 64) atomicAdd(&cnt[a.ids[p]], 1);
+  __syncthreads();
+  // lane owns experts [lane*per, (lane+1)*per)
+  const int per = (E + 63) / 64;
+  const int e0 = lane * per;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) sum += cnt[e];
+  }
+  int tot;
+  int off = wave_excl_scan(sum, lane, &tot);
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int c = cnt[e];
+      a.offsets[e] = off;
+      cnt[e] = off;
+      off += c;
+    }
+  }
+  if (lane == 0) a.offsets[E] = tot;
+  __syncthreads();
+  scatter_chunk(a, cnt, 0, n, lane, id_bits(E));
+}
+
+// Multi-block path, phase 1: per-chunk histograms -> chunk_base[c][e].
+__global__ __launch_bounds__(256) void k_perm_hist(PermuteArgs a) {
+  extern __shared__ int hist[];
+  const int E = a.E, n = a.T * a.K, c = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int p0 = c * kChunk, p1 = min(n, p0 + kChunk);
+  for (int p = p0 + threadIdx.x; p < p1; p += 256) atomicAdd(&hist[a.ids[p]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) a.chunk_base[(size_t)c * E + e] = hist[e];
+}
+
+// Phase 2 (one block): per expert, the exclusive prefix over chunks; expert
+// offsets from a block scan of the totals; finally
+// chunk_base[c][e] <- first sorted position of chunk c's pairs of expert e.
+__global__ __launch_bounds__(1024) void k_perm_scan(PermuteArgs a, int n_chunks) {
+  __shared__ int part[1024];
+  const int E = a.E, tid = threadIdx.x;
+  const int per = (E + 1023) / 1024;
+  const int e0 = tid * per;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    int run = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const size_t q = (size_t)c * E + e;
+      const int v = a.chunk_base[q];
+      a.chunk_base[q] = run;
+      run += v;
+    }
+    a.offsets[e] = run;  // count for now, rewritten below by this same thread
+    sum += run;
+  }
+  part[tid] = sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int off = part[tid] - sum;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    const int cnt = a.offsets[e];
+    a.offsets[e] = off;
+    for (int c = 0; c < n_chunks; ++c) a.chunk_base[(size_t)c * E + e] += off;
+    off += cnt;
+  }
+  if (tid == 1023) a.offsets[E] = part[1023];
+}
+
+__global__ __launch_bounds__(64) void k_perm_scatter(PermuteArgs a) {
+  extern __shared__ int running[];
+  const int E = a.E, n = a.T * a.K, c = blockIdx.x, lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) running[e] = a.chunk_base[(size_t)c * E + e];
+  __syncthreads();
+  const int p0 = c * kChunk, p1 = min(n, p0 + kChunk);
+  scatter_chunk(a, running, p0, p1, lane, id_bits(E));
+}
+
+size_t permute_scratch_ints(int T, int K, int E) {
+  const size_t n = (size_t)T * K;
+  if (n <= (size_t)kSmallMaxPairs) return 0;
+  const size_t chunks = (n + kChunk - 1) / kChunk;
+  return chunks * (size_t)E;
+}
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  const int n = a.T * a.K;
+  if (n <= kSmallMaxPairs) {
+    k_perm_small<<<1, 64, (size_t)a.E * 4, s>>>(a);
+    return hipGetLastError();
+  }
+  const int chunks = (n + kChunk - 1) / kChunk;
+  k_perm_hist<<<chunks, 256, (size_t)a.E * 4, s>>>(a);
+  k_perm_scan<<<1, 1024, 0, s>>>(a, chunks);
+  k_perm_scatter<<<chunks, 64, (size_t)a.E * 4, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

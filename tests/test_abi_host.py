@@ -1,0 +1,139 @@
+"""The C ABI library loads, exports every declared symbol, and validates
+arguments on the host before touching the device (CPU only: every call here
+returns before any kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_router_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(api.LIB_PATH), reason="libmoe.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_router_topk", "moe_permute", "moe_expert_ffn_q", "moe_combine", "moe_layer_forward"):
+        assert n in names
+    assert set(names) == set(api.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(api.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert api.moe_abi_version() == 1
+    for s in range(5):
+        assert api.lib().moe_status_str(s).startswith(b"MOE_")
+
+
+FAKE = 0x10000  # a non-null, aligned address that is never dereferenced here
+
+
+def layer(**kw):
+    d = dict(hidden=2048, inter=768, n_experts=512, top_k=10, qfmt=api.MOE_Q4_SYM_G32, act=api.MOE_ACT_BF16)
+    d.update(kw)
+    q = api.c_qmat(FAKE, FAKE, FAKE if d["qfmt"] == api.MOE_Q2_ASYM_G32 else None)
+    ex = api.c_experts(q, q, q, d.pop("n_routed", d["n_experts"]))
+    sh = api.c_experts(q, q, q, d.pop("n_shared", 1))
+    return api.c_layer(d["hidden"], d["inter"], d["n_experts"], d["top_k"], d["qfmt"], d["act"],
+                       d.pop("router_w", FAKE), None, ex, sh)
+
+
+def ws_bytes(L, T):
+    return api.lib().moe_workspace_bytes(ctypes.byref(L), T)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=0), api.MOE_E_ARG),
+    (dict(top_k=513), api.MOE_E_ARG),
+    (dict(hidden=2050), api.MOE_E_ARG),
+    (dict(inter=100), api.MOE_E_ARG),
+    (dict(hidden=8192), api.MOE_E_UNSUPPORTED),
+    (dict(qfmt=7), api.MOE_E_UNSUPPORTED),
+    (dict(act=5), api.MOE_E_UNSUPPORTED),
+    (dict(n_routed=511), api.MOE_E_ARG),
+    (dict(n_shared=2), api.MOE_E_UNSUPPORTED),
+    (dict(router_w=None), api.MOE_E_ARG),
+])
+def test_bad_descriptor_rejected_before_launch(kw, status):
+    L = layer(**kw)
+    lib = api.lib()
+    assert ws_bytes(L, 4) == 0
+    got = lib.moe_layer_forward(ctypes.byref(L), FAKE, 4, FAKE, None, None, None, FAKE, 1 << 40, None)
+    assert got == status
+
+
+def test_q2_requires_mins():
+    L = layer(qfmt=api.MOE_Q2_ASYM_G32)
+    assert ws_bytes(L, 1) > 0
+    L.routed.down.mins = None
+    assert ws_bytes(L, 1) == 0
+
+
+def test_token_count_rules():
+    L = layer()
+    lib = api.lib()
+    r = ctypes.byref(L)
+    assert lib.moe_layer_forward(r, FAKE, -1, FAKE, None, None, None, FAKE, 1 << 40, None) == api.MOE_E_ARG
+    # T == 0 is a no-op that needs no buffers at all
+    assert lib.moe_layer_forward(r, None, 0, None, None, None, None, None, 0, None) == api.MOE_OK
+    assert lib.moe_router_topk(r, None, 0, None, None, None, None, 0, None) == api.MOE_OK
+    assert lib.moe_expert_ffn_q(r, None, 0, None, None, None, None, None, None, None, 0, None) == api.MOE_OK
+    assert lib.moe_combine(r, None, None, None, None, 0, None, None, None, None) == api.MOE_OK
+
+
+def test_workspace_checks():
+    L = layer()
+    lib = api.lib()
+    r = ctypes.byref(L)
+    need = ws_bytes(L, 4)
+    assert need > 0 and ws_bytes(L, 8) >= need  # monotone in T
+    assert lib.moe_layer_forward(r, FAKE, 4, FAKE, None, None, None, FAKE, need - 1, None) == api.MOE_E_WORKSPACE
+    assert lib.moe_layer_forward(r, FAKE, 4, FAKE, None, None, None, None, need, None) == api.MOE_E_WORKSPACE
+    assert lib.moe_layer_forward(r, FAKE + 16, 4, FAKE, None, None, None, FAKE + 64, need, None) == api.MOE_E_ARG
+    assert lib.moe_permute(r, FAKE, 4, FAKE, FAKE, FAKE, FAKE, need - 1, None) == api.MOE_E_WORKSPACE
+
+
+def test_null_required_pointers():
+    L = layer()
+    lib = api.lib()
+    r = ctypes.byref(L)
+    need = ws_bytes(L, 2)
+    assert lib.moe_layer_forward(None, FAKE, 2, FAKE, None, None, None, FAKE, need, None) == api.MOE_E_ARG
+    assert lib.moe_layer_forward(r, None, 2, FAKE, None, None, None, FAKE, need, None) == api.MOE_E_ARG
+    assert lib.moe_router_topk(r, FAKE, 2, None, FAKE, None, FAKE, need, None) == api.MOE_E_ARG
+    assert lib.moe_combine(r, None, None, FAKE, FAKE, 2, FAKE, None, None, None) == api.MOE_E_ARG
+    assert lib.moe_combine(r, FAKE, None, FAKE, FAKE, 2, FAKE, None, FAKE, None) == api.MOE_E_ARG  # x_next w/o x
+    q = api.c_qmat(FAKE, FAKE, None)
+    assert lib.moe_dequant(ctypes.byref(q), api.MOE_Q2_ASYM_G32, 4, 32, FAKE, None) == api.MOE_E_ARG
+    assert lib.moe_dequant(ctypes.byref(q), 9, 4, 32, FAKE, None) == api.MOE_E_UNSUPPORTED
+    assert lib.moe_dequant(ctypes.byref(q), api.MOE_Q4_SYM_G32, 4, 33, FAKE, None) == api.MOE_E_ARG
+
+
+def test_stack_checks_every_layer():
+    good, bad = layer(), layer(top_k=0)
+    arr = (api.c_layer * 2)(good, bad)
+    assert api.lib().moe_stack_forward(arr, 2, FAKE, 1, None, FAKE, 1 << 40, None) == api.MOE_E_ARG
+    mixed = (api.c_layer * 2)(good, layer(hidden=1024))
+    assert api.lib().moe_stack_forward(mixed, 2, FAKE, 1, None, FAKE, 1 << 40, None) == api.MOE_E_ARG
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(api, "_lib", None)
+    monkeypatch.setattr(api, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no non-HIP fallback"):
+        api.lib()

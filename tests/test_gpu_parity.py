@@ -1,0 +1,345 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: ids bit-exact against the oracle's selection on the GPU's own fp32
+logits and bit-exact or a certified near-tie against the exact logits; the
+permutation and the dequantised weights bit-exact; router weights within 1e-6;
+y within max|dy| <= 2e-3 x RMS(y).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe_oracle as mo
+from sparse_moe_router_amd import api
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    api.lib()
+
+
+def full_check(ld, x, T=None, shared=True, strict=True):
+    """All steps through the ABI against the oracle.
+
+    strict: y must meet max|dy| <= 2e-3 x RMS(y) against the oracle's own
+    rounding of h (the bar of the layer's workloads).  Otherwise (small
+    intermediate sizes, where one rounding-boundary flip of a bf16 h moves y
+    by more than that) every flip of h is certified as a rounding-boundary
+    case and y is compared with the GPU's h fed to the oracle."""
+    spec = ld.spec
+    T = spec.tokens if T is None else T
+    L = gu.device_layer(ld)
+    xd = gu.x_dev(x, spec.act)
+    g = gu.run_steps(L, xd, T, with_shared=shared)
+    gu.check_routing(ld, x.values[:T], g)
+    gu.check_permutation(g, spec.n_experts)
+    rf, direct, flips = gu.check_y_teacher_forced(ld, x.values[:T], g)
+    gu.say(f"  teacher-forced max|dy|/rms {rf:.2e}, direct {direct:.2e}, certified h flips {flips}")
+    r = direct
+    if strict:
+        ref, r = gu.check_y(ld, x.values[:T], g)
+        ro, _ = gu.rel_err(g["expert_out"], ref["expert_out"])
+        assert ro <= TOL
+        if shared:
+            rs, _ = gu.rel_err(g["shared_out"], ref["shared_out"])
+            assert rs <= TOL
+    f = gu.run_forward(L, xd, T, x_next=True)
+    assert np.array_equal(f["ids"], g["ids"]) and np.array_equal(f["w"], g["w"])
+    if shared:
+        assert np.array_equal(f["y"], g["y"]), "layer_forward differs from the composed calls"
+    # residual stream: act(fp32(x + y)) from the GPU's own y
+    want = mo.residual_step(x.values[:T], f["y"]) if spec.act == synth.ACT_BF16 else \
+        mo.round_f32(x.values[:T].astype(np.float64) + f["y"])
+    assert np.array_equal(f["x_next"].float().numpy().astype(np.float64), want)
+    return g, r
+
+
+# ----------------------------------------------------------------------------- dequant (bit-exact)
+
+def _finite_f16():
+    b = np.arange(1 << 16, dtype=np.uint32)
+    return b[((b >> 10) & 0x1F) != 0x1F].astype(np.uint16)
+
+
+def test_dequant_q4_exhaustive():
+    sb = _finite_f16()
+    u = np.tile(np.tile(np.arange(16, dtype=np.uint8), 2), (sb.size, 1))
+    codes = synth.pack_q4(u)
+    out = torch.empty((sb.size, 32), dtype=torch.float32, device=gu.DEV)
+    c = torch.from_numpy(codes).to(gu.DEV)
+    s = torch.from_numpy(sb[:, None].view(np.int16).copy()).to(gu.DEV)
+    api.moe_dequant(c, s, None, "q4_sym_g32", sb.size, 32, out)
+    want = mo.dequant_q4(codes, sb[:, None])
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
+
+
+def test_dequant_q2_grid():
+    rng = np.random.default_rng(3)
+    sb = _finite_f16()
+    s_bits = np.concatenate([sb, rng.choice(sb, 60000)])
+    m_bits = np.concatenate([rng.choice(sb, sb.size), rng.choice(sb, 60000)])
+    u = np.tile(np.tile(np.arange(4, dtype=np.uint8), 8), (s_bits.size, 1))
+    codes = synth.pack_q2(u)
+    out = torch.empty((s_bits.size, 32), dtype=torch.float32, device=gu.DEV)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gu.DEV)
+    api.moe_dequant(t(codes), t(s_bits[:, None].view(np.int16)), t(m_bits[:, None].view(np.int16)),
+                    "q2_asym_g32", s_bits.size, 32, out)
+    want = mo.dequant_q2(codes, s_bits[:, None], m_bits[:, None])
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
+
+
+def test_dequant_real_expert_rows():
+    spec = synth.SPECS["verify"]
+    es = synth.gen_experts(spec, [7], threads=1)
+    for m, (rows, cols) in ((es.gate, (spec.inter, spec.hidden)), (es.down, (spec.hidden, spec.inter))):
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a[0]).view(np.int16) if a.dtype == np.uint16
+                                       else np.ascontiguousarray(a[0])).to(gu.DEV)
+        out = torch.empty((rows, cols), dtype=torch.float32, device=gu.DEV)
+        api.moe_dequant(t(m.codes), t(m.scales), t(m.mins), spec.qfmt, rows, cols, out)
+        want = mo.dequant_q2(m.codes[0], m.scales[0], m.mins[0])
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
+
+
+# ----------------------------------------------------------------------------- the tiny workload
+
+def test_tiny_config():
+    spec = synth.SPECS["tiny"]
+    ld = synth.gen_layer(spec)
+    x = synth.gen_x(spec)
+    gu.say("tiny: H64 E8 K2 I128 T4 q4 f32")
+    full_check(ld, x)
+
+
+# ----------------------------------------------------------------------------- random small layers, ragged shapes
+
+CASES = [
+    # hidden, inter, E, K, T, qfmt, act, bias
+    (64, 128, 8, 2, 4, "q4_sym_g32", "bf16", True),
+    (96, 160, 13, 3, 7, "q4_sym_g32", "bf16", True),
+    (96, 160, 13, 3, 7, "q2_asym_g32", "bf16", False),
+    (32, 32, 1, 1, 3, "q4_sym_g32", "f32", False),
+    (32, 32, 1, 1, 3, "q2_asym_g32", "bf16", True),
+    (160, 96, 40, 40, 5, "q4_sym_g32", "bf16", True),       # K = E
+    (2048, 768, 16, 4, 9, "q4_sym_g32", "bf16", True),       # real row shapes, few experts
+    (2048, 768, 16, 4, 9, "q2_asym_g32", "bf16", True),
+    (4096, 96, 6, 2, 5, "q4_sym_g32", "bf16", True),         # two groups per lane
+    (4096, 96, 6, 2, 5, "q2_asym_g32", "f32", True),
+    (64, 4096, 6, 2, 5, "q2_asym_g32", "bf16", True),
+    (224, 352, 30, 6, 33, "q4_sym_g32", "bf16", True),       # many tokens per expert (NT loop)
+    (224, 352, 30, 6, 33, "q2_asym_g32", "f32", True),
+    (128, 64, 64, 8, 600, "q4_sym_g32", "bf16", True),       # 4800 pairs: multi-block permutation
+    (128, 64, 300, 7, 700, "q2_asym_g32", "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "H{}_I{}_E{}_K{}_T{}_{}_{}".format(*c[:7]))
+def test_small_layers(case):
+    h, i, e, k, t, q, act, bias = case
+    spec = synth.LayerSpec("case", h, e, k, i, t, q, act, 0.3, 1.1 if bias else None, family=50 + len(case) + h + e)
+    ld = synth.gen_layer(spec)
+    x = synth.gen_x(spec)
+    gu.say("case", case)
+    full_check(ld, x, strict=i >= 256)
+
+
+def test_no_shared_expert():
+    spec = synth.LayerSpec("noshared", 64, 8, 3, 96, 6, "q4_sym_g32", "bf16", 0.3, 1.1, family=61, n_shared=0)
+    ld = synth.gen_layer(spec)
+    x = synth.gen_x(spec)
+    L = gu.device_layer(ld)
+    g = gu.run_steps(L, gu.x_dev(x, spec.act), spec.tokens, with_shared=False)
+    gu.check_permutation(g, spec.n_experts)
+    gu.check_y(ld, x.values, g)
+    f = gu.run_forward(L, gu.x_dev(x, spec.act), spec.tokens)
+    assert np.array_equal(f["y"], g["y"])
+
+
+def test_all_tokens_on_one_expert():
+    spec = synth.LayerSpec("hot", 128, 16, 1, 64, 50, "q2_asym_g32", "bf16", 0.01, 1.1, family=62)
+    ld = synth.gen_layer(spec)
+    ld.router_b = np.zeros(16, np.float32)
+    ld.router_b[11] = 100.0
+    x = synth.gen_x(spec)
+    g, _ = full_check(ld, x, strict=False)
+    assert np.all(g["ids"] == 11) and np.all(g["w"] == 1.0)
+    assert g["offsets"][11] == 0 and g["offsets"][12] == 50
+
+
+def test_zero_tokens_is_noop():
+    spec = synth.SPECS["tiny"]
+    L = gu.device_layer(synth.gen_layer(spec))
+    y = torch.full((1, spec.hidden), 7.0, device=gu.DEV)
+    x = torch.zeros((1, spec.hidden), device=gu.DEV)
+    api.moe_layer_forward(L, x, 0, y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+def test_zero_input_gives_zero_output():
+    spec = synth.LayerSpec("zero", 64, 8, 2, 96, 5, "q2_asym_g32", "bf16", 0.3, 1.1, family=63)
+    L = gu.device_layer(synth.gen_layer(spec))
+    f = gu.run_forward(L, torch.zeros((5, 64), dtype=torch.bfloat16, device=gu.DEV), 5)
+    assert np.all(f["y"] == 0.0)
+
+
+# ----------------------------------------------------------------------------- exact GPU-side invariants
+
+def _doubled(ld):
+    def dbl(es):
+        d = es.down
+        s = (d.scales.view(np.float16) * np.float16(2)).view(np.uint16)
+        m = None if d.mins is None else (d.mins.view(np.float16) * np.float16(2)).view(np.uint16)
+        return synth.ExpertSet(es.gate, es.up, synth.PackedMat(d.codes, s, m), es.index)
+    return synth.LayerData(ld.spec, ld.layer, ld.router_w, ld.router_b, dbl(ld.routed), dbl(ld.shared))
+
+
+@pytest.mark.parametrize("qfmt", ["q4_sym_g32", "q2_asym_g32"])
+def test_power_of_two_down_scales_double_y_bitwise(qfmt):
+    spec = synth.LayerSpec("dbl", 2048, 32, 4, 768, 5, qfmt, "bf16", 0.02, 1.1, family=64)
+    ld = synth.gen_layer(spec)
+    xd = gu.x_dev(synth.gen_x(spec), spec.act)
+    a = gu.run_forward(gu.device_layer(ld), xd, 5)
+    b = gu.run_forward(gu.device_layer(_doubled(ld)), xd, 5)
+    assert np.array_equal(b["y"], 2 * a["y"])
+
+
+def test_reruns_are_bitwise_identical():
+    spec = synth.SPECS["verify"].with_tokens(5)
+    spec = synth.LayerSpec("det", 2048, 64, 10, 768, 5, "q2_asym_g32", "bf16", spec.router_std, 1.1, family=65)
+    ld = synth.gen_layer(spec)
+    L = gu.device_layer(ld)
+    xd = gu.x_dev(synth.gen_x(spec), spec.act)
+    a = gu.run_forward(L, xd, 5)
+    for _ in range(3):
+        b = gu.run_forward(L, xd, 5)
+        assert np.array_equal(a["y"], b["y"])
+
+
+def test_token_order_batch_invariance():
+    spec = synth.LayerSpec("perm", 256, 24, 4, 160, 12, "q4_sym_g32", "bf16", 0.3, 1.1, family=66)
+    ld = synth.gen_layer(spec)
+    x = synth.gen_x(spec)
+    L = gu.device_layer(ld)
+    perm = np.random.default_rng(0).permutation(12)
+    a = gu.run_forward(L, gu.x_dev(x, spec.act), 12)
+    xp = synth.Activations(x.values[perm], x.storage[perm])
+    b = gu.run_forward(L, gu.x_dev(xp, spec.act), 12)
+    assert np.array_equal(b["ids"], a["ids"][perm])
+    assert np.array_equal(b["y"], a["y"][perm])
+
+
+def test_expert_relabelling():
+    spec = synth.LayerSpec("relabel", 256, 20, 3, 96, 6, "q2_asym_g32", "bf16", 0.3, 1.1, family=67)
+    ld = synth.gen_layer(spec)
+    x = synth.gen_x(spec)
+    perm = np.random.default_rng(1).permutation(20)
+    inv = np.argsort(perm)
+    moved = synth.subset(ld.routed, inv)
+    moved.index = np.arange(20)
+    ld2 = synth.LayerData(spec, 0, ld.router_w[inv].copy(), ld.router_b[inv].copy(), moved, ld.shared)
+    xd = gu.x_dev(x, spec.act)
+    a = gu.run_forward(gu.device_layer(ld), xd, 6)
+    b = gu.run_forward(gu.device_layer(ld2), xd, 6)
+    assert np.array_equal(b["ids"], perm[a["ids"]])
+    assert np.array_equal(b["y"], a["y"])
+
+
+# ----------------------------------------------------------------------------- the full-size workloads
+
+@pytest.fixture(scope="module")
+def family1():
+    spec = synth.SPECS["decode"]
+    gu.say("generating the 512-expert 4-bit layer")
+    ld = synth.gen_layer(spec)
+    return ld, gu.device_layer(ld)
+
+
+def test_decode_layer(family1):
+    ld, L = family1
+    spec = synth.SPECS["decode"]
+    x = synth.gen_x(spec)
+    xd = gu.x_dev(x, spec.act)
+    gu.say("decode: T1 E512 K10 H2048 I768 q4")
+    g = gu.run_steps(L, xd, 1)
+    gu.check_routing(ld, x.values, g)
+    gu.check_permutation(g, 512)
+    _, r = gu.check_y(ld, x.values, g)
+    gu.say(f"decode max|dy|/rms = {r:.2e}")
+    f = gu.run_forward(L, xd, 1)
+    assert np.array_equal(f["y"], g["y"])
+
+
+def test_decode_many_inputs(family1):
+    """Decode at 16 different tokens, one at a time (each through its own layer call)."""
+    ld, L = family1
+    spec = synth.SPECS["decode"]
+    x = synth.gen_x(spec, tokens=16)
+    xd = gu.x_dev(x, spec.act)
+    worst = 0.0
+    for t in range(16):
+        f = gu.run_forward(L, xd[t:t + 1].contiguous(), 1)
+        ref = mo.layer_forward(ld, x.values[t:t + 1], ids=f["ids"])
+        r, _ = gu.rel_err(f["y"], ref["y"])
+        worst = max(worst, r)
+    gu.say(f"decode x16 worst max|dy|/rms = {worst:.2e}")
+    assert worst <= TOL
+
+
+def test_prefill_sampled(family1):
+    ld, L = family1
+    spec = synth.SPECS["prefill"]
+    x = synth.gen_x(spec)
+    xd = gu.x_dev(x, spec.act)
+    gu.say("prefill: T4096 E512 K10 q4")
+    g = gu.run_steps(L, xd, spec.tokens)
+    # properties at full size
+    counts = np.bincount(g["ids"].reshape(-1), minlength=512)
+    assert np.array_equal(np.diff(g["offsets"]), counts)
+    gu.check_permutation(g, 512)
+    tokens = np.random.default_rng(2).choice(spec.tokens, 12, replace=False)
+    gu.check_routing(ld, x.values, g, tokens=tokens)
+    _, r = gu.check_y(ld, x.values, g, tokens=tokens)
+    gu.say(f"prefill sampled max|dy|/rms = {r:.2e}; distinct experts {int((counts > 0).sum())}, max load {counts.max()}")
+    f = gu.run_forward(L, xd, spec.tokens)
+    assert np.array_equal(f["ids"], g["ids"])
+    assert np.array_equal(f["y"], g["y"])
+
+
+def test_verify_layer():
+    spec = synth.SPECS["verify"]
+    ld = synth.gen_layer(spec)
+    x = synth.gen_x(spec)
+    gu.say("verify: T5 E512 K10 q2")
+    g, r = full_check(ld, x)
+    gu.say(f"verify max|dy|/rms = {r:.2e}; distinct experts {len(np.unique(g['ids']))}")
+
+
+def test_split_expert_calls_match_ffn():
+    """moe_expert_gate_up_q then moe_expert_down_q == moe_expert_ffn_q, bitwise."""
+    spec = synth.LayerSpec("split", 2048, 48, 6, 768, 7, "q2_asym_g32", "bf16", 0.0221, 1.1, family=68)
+    ld = synth.gen_layer(spec)
+    x = synth.gen_x(spec)
+    L = gu.device_layer(ld)
+    xd = gu.x_dev(x, spec.act)
+    g = gu.run_steps(L, xd, 7)
+    dev = gu.DEV
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    off, sp = t(g["offsets"]), t(g["sorted_pairs"])
+    h = torch.empty((42, 768), dtype=torch.bfloat16, device=dev)
+    hs = torch.empty((7, 768), dtype=torch.bfloat16, device=dev)
+    api.moe_expert_gate_up_q(L, xd, 7, off, sp, h, hs)
+    o = torch.empty((42, 2048), dtype=torch.float32, device=dev)
+    so = torch.empty((7, 2048), dtype=torch.float32, device=dev)
+    api.moe_expert_down_q(L, h, hs, 7, off, o, so)
+    torch.cuda.synchronize()
+    assert np.array_equal(h.float().cpu().numpy(), g["h"])
+    assert np.array_equal(hs.float().cpu().numpy(), g["shared_h"])
+    assert np.array_equal(o.cpu().numpy(), g["expert_out"])
+    assert np.array_equal(so.cpu().numpy(), g["shared_out"])
