@@ -106,16 +106,16 @@ def main():
     log(f"decode: {ms_per_step * 1e3:.2f} us/step, {tok_s:.0f} tok/s")
 
     # routing of each copy for its first timed token: distinct experts per step
-    ids = torch.empty((1, K), dtype=torch.int32, device=dev)
     wts = torch.empty((1, K), dtype=torch.float32, device=dev)
+    idss = [torch.empty((1, K), dtype=torch.int32, device=dev) for _ in range(args.copies)]
     offs = [torch.empty(E + 1, dtype=torch.int32, device=dev) for _ in range(args.copies)]
     sps = [torch.empty(K, dtype=torch.int32, device=dev) for _ in range(args.copies)]
     pp = torch.empty(K, dtype=torch.int32, device=dev)
     distinct = []
     for c in range(args.copies):
-        api.moe_router_topk(layers[c], xs[c:c + 1], 1, ids, wts, ws=ws)
-        api.moe_permute(layers[c], ids, 1, offs[c], sps[c], pp, ws)
-        distinct.append(len(set(ids.cpu().numpy().reshape(-1).tolist())))
+        api.moe_router_topk(layers[c], xs[c:c + 1], 1, idss[c], wts, ws=ws)
+        api.moe_permute(layers[c], idss[c], 1, offs[c], sps[c], pp, ws)
+        distinct.append(len(set(idss[c].cpu().numpy().reshape(-1).tolist())))
     u_mean = float(np.mean(distinct))
 
     # dominant kernel: expert gate/up + SwiGLU (one kernel per call), timed
@@ -124,12 +124,12 @@ def main():
     hs = torch.empty((1, I), dtype=torch.bfloat16, device=dev)
     for r in range(50):
         c = r % args.copies
-        api.moe_expert_gate_up_q(layers[c], xs[c:c + 1], 1, offs[c], sps[c], h, hs, stream=stream)
+        api.moe_expert_gate_up_q(layers[c], xs[c:c + 1], 1, idss[c], offs[c], sps[c], h, hs, stream=stream)
     torch.cuda.synchronize()
     start.record(stream)
     for r in range(args.kernel_reps):
         c = r % args.copies
-        api.moe_expert_gate_up_q(layers[c], xs[c:c + 1], 1, offs[c], sps[c], h, hs, stream=stream)
+        api.moe_expert_gate_up_q(layers[c], xs[c:c + 1], 1, idss[c], offs[c], sps[c], h, hs, stream=stream)
     end.record(stream)
     torch.cuda.synchronize()
     k_us = start.elapsed_time(end) * 1e3 / args.kernel_reps

@@ -124,8 +124,9 @@ moe_status moe_permute(const moe_layer *layer, const int32_t *topk_ids, int32_t 
                        void *ws, size_t ws_bytes, void *stream);
 
 /* Expert FFNs on the permuted pairs: for sorted position j with pair
- * p = sorted_pairs[j], token t = p / K and expert e (expert_offsets[e] <= j <
- * expert_offsets[e+1]):
+ * p = sorted_pairs[j], token t = p / K and expert e = topk_ids[p]
+ * (expert_offsets[e] <= j < expert_offsets[e+1]), i.e. the outputs of
+ * moe_router_topk and moe_permute:
  *   h = round_act(silu(W_g[e] x_t) * (W_u[e] x_t)),  silu(z) = z / (1 + exp(-z))
  *   expert_out[j] = W_d[e] h                         (fp32, [T*K][H])
  * and, if the layer has a shared expert and shared_out_opt != NULL, the same
@@ -136,7 +137,7 @@ moe_status moe_permute(const moe_layer *layer, const int32_t *topk_ids, int32_t 
  * receive the intermediate activations h if non-NULL (otherwise they live in
  * the workspace); shared_h_opt is only written when shared_out_opt is given.
  * Workspace: at least moe_workspace_bytes(layer, T). */
-moe_status moe_expert_ffn_q(const moe_layer *layer, const void *x, int32_t T,
+moe_status moe_expert_ffn_q(const moe_layer *layer, const void *x, int32_t T, const int32_t *topk_ids,
                             const int32_t *expert_offsets, const int32_t *sorted_pairs,
                             float *expert_out, float *shared_out_opt,
                             void *h_opt, void *shared_h_opt,
@@ -145,18 +146,19 @@ moe_status moe_expert_ffn_q(const moe_layer *layer, const void *x, int32_t T,
 /* The two halves of moe_expert_ffn_q, one kernel each.
  * moe_expert_gate_up_q: h[j] = round_act(silu(W_g[e] x_t) * (W_u[e] x_t)) for
  *   every sorted position j (h [T*K][I] act type), and for the shared expert
- *   shared_h_opt[t] ([T][I]) if non-NULL and the layer has one.  Reads
- *   expert_offsets and sorted_pairs (token t = sorted_pairs[j] / K).
+ *   shared_h_opt[t] ([T][I]) if non-NULL and the layer has one.
  * moe_expert_down_q: expert_out[j] = W_d[e] h[j] ([T*K][H] fp32), and
  *   shared_out_opt[t] = W_d^shared shared_h_opt[t] if shared_out_opt is given
- *   (then shared_h_opt is required).  Only expert_offsets is read.
+ *   (then shared_h_opt is required).
+ * Both read topk_ids, expert_offsets and sorted_pairs as moe_expert_ffn_q does.
  * No workspace.  (Rows "fused dequant gate/up + SwiGLU" and "fused dequant down
  * projection" of the expert sub-network, page 2 "Layer 1".) */
-moe_status moe_expert_gate_up_q(const moe_layer *layer, const void *x, int32_t T,
+moe_status moe_expert_gate_up_q(const moe_layer *layer, const void *x, int32_t T, const int32_t *topk_ids,
                                 const int32_t *expert_offsets, const int32_t *sorted_pairs,
                                 void *h, void *shared_h_opt, void *stream);
 moe_status moe_expert_down_q(const moe_layer *layer, const void *h, const void *shared_h_opt, int32_t T,
-                             const int32_t *expert_offsets, float *expert_out, float *shared_out_opt,
+                             const int32_t *topk_ids, const int32_t *expert_offsets,
+                             const int32_t *sorted_pairs, float *expert_out, float *shared_out_opt,
                              void *stream);
 
 /* Weighted combine:

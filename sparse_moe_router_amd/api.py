@@ -64,9 +64,9 @@ def lib() -> ctypes.CDLL:
         sigs = {
             "moe_router_topk": [lp, vp, i32, vp, vp, vp, vp, sz, vp],
             "moe_permute": [lp, vp, i32, vp, vp, vp, vp, sz, vp],
-            "moe_expert_ffn_q": [lp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
-            "moe_expert_gate_up_q": [lp, vp, i32, vp, vp, vp, vp, vp],
-            "moe_expert_down_q": [lp, vp, vp, i32, vp, vp, vp, vp],
+            "moe_expert_ffn_q": [lp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_expert_gate_up_q": [lp, vp, i32, vp, vp, vp, vp, vp, vp],
+            "moe_expert_down_q": [lp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
             "moe_combine": [lp, vp, vp, vp, vp, i32, vp, vp, vp, vp],
             "moe_layer_forward": [lp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
             "moe_stack_forward": [lp, i32, vp, i32, vp, vp, sz, vp],
@@ -202,10 +202,10 @@ def moe_permute(layer: Layer, topk_ids, T, expert_offsets, sorted_pairs, pair_po
                                             _ptr(pair_pos, torch.int32), w, wn, _stream(stream)))
 
 
-def moe_expert_ffn_q(layer: Layer, x, T, expert_offsets, sorted_pairs, expert_out, shared_out=None, h=None,
-                     shared_h=None, ws=None, stream=None):
+def moe_expert_ffn_q(layer: Layer, x, T, topk_ids, expert_offsets, sorted_pairs, expert_out, shared_out=None,
+                     h=None, shared_h=None, ws=None, stream=None):
     w, wn = _ws(ws)
-    _check("moe_expert_ffn_q", lib().moe_expert_ffn_q(layer.ref, _x(layer, x, T), int(T),
+    _check("moe_expert_ffn_q", lib().moe_expert_ffn_q(layer.ref, _x(layer, x, T), int(T), _ptr(topk_ids, torch.int32),
                                                       _ptr(expert_offsets, torch.int32),
                                                       _ptr(sorted_pairs, torch.int32),
                                                       _ptr(expert_out, torch.float32),
@@ -214,18 +214,23 @@ def moe_expert_ffn_q(layer: Layer, x, T, expert_offsets, sorted_pairs, expert_ou
                                                       w, wn, _stream(stream)))
 
 
-def moe_expert_gate_up_q(layer: Layer, x, T, expert_offsets, sorted_pairs, h, shared_h=None, stream=None):
+def moe_expert_gate_up_q(layer: Layer, x, T, topk_ids, expert_offsets, sorted_pairs, h, shared_h=None,
+                         stream=None):
     _check("moe_expert_gate_up_q", lib().moe_expert_gate_up_q(layer.ref, _x(layer, x, T), int(T),
+                                                              _ptr(topk_ids, torch.int32),
                                                               _ptr(expert_offsets, torch.int32),
                                                               _ptr(sorted_pairs, torch.int32),
                                                               _ptr(h, layer.act_dtype),
                                                               _ptr(shared_h, layer.act_dtype), _stream(stream)))
 
 
-def moe_expert_down_q(layer: Layer, h, shared_h, T, expert_offsets, expert_out, shared_out=None, stream=None):
+def moe_expert_down_q(layer: Layer, h, shared_h, T, topk_ids, expert_offsets, sorted_pairs, expert_out,
+                      shared_out=None, stream=None):
     _check("moe_expert_down_q", lib().moe_expert_down_q(layer.ref, _ptr(h, layer.act_dtype),
                                                         _ptr(shared_h, layer.act_dtype), int(T),
+                                                        _ptr(topk_ids, torch.int32),
                                                         _ptr(expert_offsets, torch.int32),
+                                                        _ptr(sorted_pairs, torch.int32),
                                                         _ptr(expert_out, torch.float32),
                                                         _ptr(shared_out, torch.float32), _stream(stream)))
 

@@ -9,21 +9,37 @@ namespace moe {
 
 // One thread per 4 consecutive outputs of one token; fixed summation order, so
 // the result is bitwise reproducible.
+constexpr int kSlotBatch = 12;  // slots whose loads are issued together
+
 template <int ACT>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int h4 = a.H >> 2;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)a.T * h4) return;
   const int t = (int)(idx / h4), j4 = (int)(idx % h4);
-  float4 acc = a.so ? reinterpret_cast<const float4*>(a.so)[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k = 0; k < a.K; ++k) {
-    const int p = a.pair_pos[(size_t)t * a.K + k];
-    const float w = a.w[(size_t)t * a.K + k];
-    const float4 o = reinterpret_cast<const float4*>(a.o)[(size_t)p * h4 + j4];
-    acc.x = fmaf(w, o.x, acc.x);
-    acc.y = fmaf(w, o.y, acc.y);
-    acc.z = fmaf(w, o.z, acc.z);
-    acc.w = fmaf(w, o.w, acc.w);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < a.K; k0 += kSlotBatch) {
+    int pos[kSlotBatch];
+    float w[kSlotBatch];
+    float4 o[kSlotBatch];
+#pragma unroll
+    for (int i = 0; i < kSlotBatch; ++i) {  // clamped slot: loads outside conditional blocks
+      const size_t q = (size_t)t * a.K + min(k0 + i, a.K - 1);
+      pos[i] = a.pair_pos[q];
+      w[i] = a.w[q];
+    }
+#pragma unroll
+    for (int i = 0; i < kSlotBatch; ++i) o[i] = reinterpret_cast<const float4*>(a.o)[(size_t)pos[i] * h4 + j4];
+    if (k0 == 0 && a.so) acc = reinterpret_cast<const float4*>(a.so)[idx];  // the shared expert comes first
+#pragma unroll
+    for (int i = 0; i < kSlotBatch; ++i) {
+      if (k0 + i < a.K) {
+        acc.x = fmaf(w[i], o[i].x, acc.x);
+        acc.y = fmaf(w[i], o[i].y, acc.y);
+        acc.z = fmaf(w[i], o[i].z, acc.z);
+        acc.w = fmaf(w[i], o[i].w, acc.w);
+      }
+    }
   }
   reinterpret_cast<float4*>(a.y)[idx] = acc;
   if (a.x_next) {

@@ -8,206 +8,34 @@
 // expert's tokens.  A row's 32-element groups are spread over LPR lanes (one
 // group per lane at H = 2048: each lane loads 16 B of 4-bit codes and one fp16
 // scale per row); partial dot products are reduced over those LPR lanes.
-//
-// Inner product of one group (bf16 activations): each code u becomes the exact
-// bf16 number 128 + u by OR-ing it into the mantissa of 0x4300 (=128), two
-// codes per 32-bit word, and v_dot2_f32_bf16 multiplies the pair with a pair
-// of activations in fp32 (products of an 8-bit code and a bf16 value are exact
-// in fp32).  The offset is removed with a per-group constant computed once per
-// token:  sum (u - 8) x = sum (128 + u) x - 136 sum x   (4-bit),
-//         sum u x       = sum (128 + u) x - 128 sum x   (2-bit),
-// and the group scale (and 2-bit minimum) is applied once per group:
-//         acc += s * sum(q x)            (4-bit, w = s q)
-//         acc += s * sum(u x) + m sum x  (2-bit, w = s u + m).
-// Activation pairs are pre-arranged per token to match the code pairs a mask
-// and a shift produce: 4-bit word i of a group yields pairs (8i+j, 8i+4+j) for
-// j = 0..3 from nibbles j and j+4; 2-bit word i yields pairs (16i+j, 16i+8+j)
-// for j = 0..7 from crumbs j and j+8.
-#include "moe_device.h"
-#include "moe_internal.h"
+#include "gemv_tile.h"
+#include "topk.h"
 
 namespace moe {
 
-template <int QF> struct CodeOf;
-template <> struct CodeOf<MOE_Q4_SYM_G32> { using T = uint4; static constexpr int kBytes = 16; };
-template <> struct CodeOf<MOE_Q2_ASYM_G32> { using T = uint2; static constexpr int kBytes = 8; };
-
-// Prepared activations of one 32-element group of one token.
-template <int QF, int ACT> struct XGroup;
-
-template <int QF> struct XGroup<QF, MOE_ACT_BF16> {
-  uint32_t p[16];  // bf16 pairs matching the code pairs
-  float c;         // 136 * sum x (4-bit) or 128 * sum x (2-bit)
-  float sx;        // sum x (2-bit only)
-
-  __device__ __forceinline__ void load(const void* base, size_t elem) {
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
-    uint4 q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = src[i];
-    if constexpr (QF == MOE_Q4_SYM_G32) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {  // elements 8i..8i+7 in q[i]
-        p[4 * i + 0] = (q[i].x & 0xffffu) | (q[i].z << 16);
-        p[4 * i + 1] = (q[i].x >> 16) | (q[i].z & 0xffff0000u);
-        p[4 * i + 2] = (q[i].y & 0xffffu) | (q[i].w << 16);
-        p[4 * i + 3] = (q[i].y >> 16) | (q[i].w & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {  // elements 16i..16i+7 in q[2i], 16i+8..16i+15 in q[2i+1]
-        const uint32_t a[4] = {q[2 * i].x, q[2 * i].y, q[2 * i].z, q[2 * i].w};
-        const uint32_t b[4] = {q[2 * i + 1].x, q[2 * i + 1].y, q[2 * i + 1].z, q[2 * i + 1].w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          p[8 * i + 2 * m] = (a[m] & 0xffffu) | (b[m] << 16);
-          p[8 * i + 2 * m + 1] = (a[m] >> 16) | (b[m] & 0xffff0000u);
-        }
-      }
-    }
-    constexpr uint32_t kOff = (QF == MOE_Q4_SYM_G32) ? 0x43084308u : 0x43004300u;  // (136,136) / (128,128)
-    float c0 = 0.f, c1 = 0.f, s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      c0 = dot2_bf16(kOff, p[i], c0);
-      c1 = dot2_bf16(kOff, p[i + 1], c1);
-      if constexpr (QF == MOE_Q2_ASYM_G32) {
-        s0 = dot2_bf16(0x3f803f80u, p[i], s0);
-        s1 = dot2_bf16(0x3f803f80u, p[i + 1], s1);
-      }
-    }
-    c = c0 + c1;
-    sx = s0 + s1;
-  }
-};
-
-template <int QF> struct XGroup<QF, MOE_ACT_F32> {
-  float v[32];
-  float sx;
-  __device__ __forceinline__ void load(const void* base, size_t elem) {
-    const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 f = src[i];
-      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
-      s += (f.x + f.y) + (f.z + f.w);
-    }
-    sx = s;
-  }
-};
-
-// sum over the group of q*x (4-bit, q = u - 8) or u*x (2-bit).
-template <int QF, int ACT>
-__device__ __forceinline__ float group_dot(const typename CodeOf<QF>::T& cw, const XGroup<QF, ACT>& x) {
-  if constexpr (ACT == MOE_ACT_BF16) {
-    float d0 = 0.f, d1 = 0.f;
-    if constexpr (QF == MOE_Q4_SYM_G32) {
-      const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        d0 = dot2_bf16((w[i] & 0x000f000fu) | 0x43004300u, x.p[4 * i + 0], d0);
-        d1 = dot2_bf16(((w[i] >> 4) & 0x000f000fu) | 0x43004300u, x.p[4 * i + 1], d1);
-        d0 = dot2_bf16(((w[i] >> 8) & 0x000f000fu) | 0x43004300u, x.p[4 * i + 2], d0);
-        d1 = dot2_bf16(((w[i] >> 12) & 0x000f000fu) | 0x43004300u, x.p[4 * i + 3], d1);
-      }
-    } else {
-      const uint32_t w[2] = {cw.x, cw.y};
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          d0 = dot2_bf16(((w[i] >> (2 * j)) & 0x00030003u) | 0x43004300u, x.p[8 * i + j], d0);
-          d1 = dot2_bf16(((w[i] >> (2 * j + 2)) & 0x00030003u) | 0x43004300u, x.p[8 * i + j + 1], d1);
-        }
-      }
-    }
-    return (d0 + d1) - x.c;
-  } else {
-    float d0 = 0.f, d1 = 0.f;
-    if constexpr (QF == MOE_Q4_SYM_G32) {
-      const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          d0 = fmaf((float)((int)((w[i] >> (4 * j)) & 15u) - 8), x.v[8 * i + j], d0);
-          d1 = fmaf((float)((int)((w[i] >> (4 * j + 4)) & 15u) - 8), x.v[8 * i + j + 1], d1);
-        }
-      }
-    } else {
-      const uint32_t w[2] = {cw.x, cw.y};
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          d0 = fmaf((float)((w[i] >> (2 * j)) & 3u), x.v[16 * i + j], d0);
-          d1 = fmaf((float)((w[i] >> (2 * j + 2)) & 3u), x.v[16 * i + j + 1], d1);
-        }
-      }
-    }
-    return d0 + d1;
-  }
-}
-
-template <int QF, int ACT>
-__device__ __forceinline__ float group_acc(float acc, const typename CodeOf<QF>::T& cw, uint16_t s16, uint16_t m16,
-                                           const XGroup<QF, ACT>& x) {
-  const float d = group_dot<QF, ACT>(cw, x);
-  acc = fmaf(f16_to_f32(s16), d, acc);
-  if constexpr (QF == MOE_Q2_ASYM_G32) acc = fmaf(f16_to_f32(m16), x.sx, acc);
-  return acc;
-}
-
-struct MatView {
-  const uint8_t* codes;
-  const uint16_t* scales;
-  const uint16_t* mins;
-  size_t row_bytes;  // code bytes per row
-  int groups;        // groups per row
-};
-
-template <int QF>
-__device__ __forceinline__ MatView expert_view(const QMat& m, int e, int rows, int cols) {
-  MatView v;
-  v.row_bytes = (size_t)cols * (QF == MOE_Q4_SYM_G32 ? 4 : 2) / 8;
-  v.groups = cols / kGroup;
-  v.codes = m.codes + (size_t)e * rows * v.row_bytes;
-  v.scales = m.scales + (size_t)e * rows * v.groups;
-  v.mins = m.mins ? m.mins + (size_t)e * rows * v.groups : nullptr;
-  return v;
-}
-
 // Which token list a block works on: a routed expert (its slice of the sorted
-// pairs) or the shared expert (all tokens).  Routed blocks are found without a
-// list of active experts: block y visits sorted positions y, y + ny, ... and
-// takes the expert whose slice starts at that position (a binary search of
-// expert_offsets gives the expert holding a position; an expert is visited by
-// exactly one block, the one whose y matches its first position modulo ny).
+// pairs) or the shared expert (all tokens).  Block row y visits sorted
+// positions y, y + ny, ... and takes the expert whose slice starts there (the
+// expert of position j is ids[sorted_pairs[j]]), so each expert is handled by
+// exactly one block row and needs two dependent loads to find.
 struct Work {
   int expert;   // routed expert id, or -1 for the shared expert
   int lo, n;    // sorted positions [lo, lo + n) or tokens [0, n)
+  int pair0;    // sorted_pairs[lo] (routed)
 };
 
-__device__ __forceinline__ int expert_at(const int32_t* offsets, int E, int pos) {
-  int lo = 0, hi = E;  // largest e with offsets[e] <= pos
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (offsets[mid] <= pos) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
-// Next routed expert for this block at or after sorted position *pos (step
-// ny); returns false when the block has none left.
 __device__ __forceinline__ bool next_routed(const FfnArgs& a, int ny, int* pos, Work* w) {
   const int n = a.T * a.K;
   for (; *pos < n; *pos += ny) {
-    const int e = expert_at(a.offsets, a.E, *pos);
-    if (a.offsets[e] == *pos) {
+    const int j = *pos;
+    const int pj = a.sorted_pairs[j];
+    const int pp = j > 0 ? a.sorted_pairs[j - 1] : pj;
+    const int e = a.ids[pj];
+    if (j == 0 || a.ids[pp] != e) {
       w->expert = e;
-      w->lo = *pos;
-      w->n = a.offsets[e + 1] - *pos;
+      w->lo = j;
+      w->pair0 = pj;
+      w->n = a.offsets[e + 1] - j;
       *pos += ny;
       return true;
     }
@@ -215,78 +43,70 @@ __device__ __forceinline__ bool next_routed(const FfnArgs& a, int ny, int* pos, 
   return false;
 }
 
-// gate/up + SwiGLU:  h[j][r] = round_act(silu(Wg[r].x_t) * (Wu[r].x_t))
-template <int QF, int ACT, int NT, int GPL, int RPW>
-__global__ __launch_bounds__(256) void k_gateup(FfnArgs a, int ny, int lpr_log2) {
-  using CT = typename CodeOf<QF>::T;
-  const bool shared = (int)blockIdx.y == ny;  // the extra last row of blocks
-  int pos = blockIdx.y;
-  Work wk;
-  if (shared) { wk.expert = -1; wk.lo = 0; wk.n = a.T; }
-  else if (!next_routed(a, ny, &pos, &wk)) return;
- for (;;) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
-  const int sub = lane & (LPR - 1), rsub = lane >> lpr_log2;
-  const int G = a.H / kGroup;
-  const MatView vg = expert_view<QF>(shared ? a.sgate : a.gate, shared ? 0 : wk.expert, a.I, a.H);
-  const MatView vu = expert_view<QF>(shared ? a.sup : a.up, shared ? 0 : wk.expert, a.I, a.H);
-  void* out = shared ? a.hs : a.h;
-  const int r0 = (blockIdx.x * 4 + wave) * RPW * RPI + rsub;
+// Occupancy the register budget is sized for: the decode shapes (one token
+// chunk, one group per lane) fit four waves per SIMD.
+constexpr int waves_per_simd(int act, int nt, int gpl) {
+  return (act == MOE_ACT_BF16 && gpl == 1) ? (nt == 1 ? 4 : 2) : 1;
+}
 
-  for (int c0 = 0; c0 < wk.n; c0 += NT) {
-    const int nt = min(NT, wk.n - c0);
-    XGroup<QF, ACT> xg[NT][GPL];
+// gate/up + SwiGLU of one expert (or the shared expert) for the wave's RPW
+// rows:  h[j][r] = round_act(silu(Wg[r].x_t) * (Wu[r].x_t)).  The activations
+// of the first chunk of tokens, then the weights, are all requested before the
+// first arithmetic (the memory counter completes in issue order); the weight
+// rows are loaded once and reused for every chunk of NT tokens.  tok(jj) gives
+// the token of the expert's jj-th pair.
+template <int QF, int ACT, int NT, int GPL, int RPW, typename TokFn>
+__device__ __forceinline__ void gateup_rows(const FfnArgs& a, const Work& wk, bool shared, int rbase, int rsub,
+                                            int sub, int lpr_log2, TokFn tok) {
+  const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
+  const int G = a.H / kGroup;
+  const int r0 = rbase + rsub;
+  bool gok[GPL];
+#pragma unroll
+  for (int gi = 0; gi < GPL; ++gi) gok[gi] = sub + gi * LPR < G;
+  void* out = shared ? a.hs : a.h;
+  XGroup<QF, ACT> xg[NT][GPL];
+  auto load_x = [&](int c0) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      if (j < nt) {
-        const int tok = shared ? c0 + j : a.sorted_pairs[wk.lo + c0 + j] / a.K;
+      const int jj = c0 + min(j, wk.n - 1 - c0);  // clamped: duplicates past the end
+      const int t = tok(jj);
 #pragma unroll
-        for (int gi = 0; gi < GPL; ++gi) {
-          const int g = sub + gi * LPR;
-          if (g < G) xg[j][gi].load(a.x, (size_t)tok * a.H + (size_t)g * kGroup);
-        }
-      }
+      for (int gi = 0; gi < GPL; ++gi)
+        xg[j][gi].load_raw(a.x, (size_t)t * a.H + (size_t)min(sub + gi * LPR, G - 1) * kGroup);
     }
-    // issue every row's loads before any arithmetic
-    CT cg[RPW][GPL], cu[RPW][GPL];
-    uint16_t sg[RPW][GPL], su[RPW][GPL], mg[RPW][GPL], mu[RPW][GPL];
+  };
+  load_x(0);
+  __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weight loads
+  const MatView vg = expert_view<QF>(shared ? a.sgate : a.gate, shared ? 0 : wk.expert, a.I, a.H);
+  const MatView vu = expert_view<QF>(shared ? a.sup : a.up, shared ? 0 : wk.expert, a.I, a.H);
+  RowTile<QF, RPW, GPL> tg, tu;
+  tg.load(vg, rbase, rsub, RPI, a.I, sub, LPR);
+  tu.load(vu, rbase, rsub, RPI, a.I, sub, LPR);
+  __builtin_amdgcn_sched_barrier(0);  // ... and every load issued before the arithmetic
+  for (int c0 = 0; c0 < wk.n; c0 += NT) {
+    const int nt = min(NT, wk.n - c0);
+    if (c0 > 0) load_x(c0);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int gi = 0; gi < GPL; ++gi) xg[j][gi].prep();
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
-      const int r = r0 + rr * RPI;
-#pragma unroll
-      for (int gi = 0; gi < GPL; ++gi) {
-        const int g = sub + gi * LPR;
-        if (r < a.I && g < G) {
-          cg[rr][gi] = *reinterpret_cast<const CT*>(vg.codes + (size_t)r * vg.row_bytes + (size_t)g * CodeOf<QF>::kBytes);
-          cu[rr][gi] = *reinterpret_cast<const CT*>(vu.codes + (size_t)r * vu.row_bytes + (size_t)g * CodeOf<QF>::kBytes);
-          sg[rr][gi] = vg.scales[(size_t)r * G + g];
-          su[rr][gi] = vu.scales[(size_t)r * G + g];
-          if constexpr (QF == MOE_Q2_ASYM_G32) {
-            mg[rr][gi] = vg.mins[(size_t)r * G + g];
-            mu[rr][gi] = vu.mins[(size_t)r * G + g];
-          } else {
-            mg[rr][gi] = 0; mu[rr][gi] = 0;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
+      __builtin_amdgcn_sched_barrier(0);  // one row at a time: unpacked codes stay few
       const int r = r0 + rr * RPI;
       float ga[NT], ua[NT];
 #pragma unroll
       for (int j = 0; j < NT; ++j) { ga[j] = 0.f; ua[j] = 0.f; }
 #pragma unroll
       for (int gi = 0; gi < GPL; ++gi) {
-        const int g = sub + gi * LPR;
-        if (r < a.I && g < G) {
 #pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            if (j < nt) {
-              ga[j] = group_acc<QF, ACT>(ga[j], cg[rr][gi], sg[rr][gi], mg[rr][gi], xg[j][gi]);
-              ua[j] = group_acc<QF, ACT>(ua[j], cu[rr][gi], su[rr][gi], mu[rr][gi], xg[j][gi]);
-            }
+        for (int j = 0; j < NT; ++j) {
+          if (j < nt) {
+            const float g1 = group_acc<QF, ACT>(ga[j], tg.c[rr][gi], tg.s[rr][gi], tg.m[rr][gi], xg[j][gi]);
+            const float u1 = group_acc<QF, ACT>(ua[j], tu.c[rr][gi], tu.s[rr][gi], tu.m[rr][gi], xg[j][gi]);
+            ga[j] = gok[gi] ? g1 : ga[j];
+            ua[j] = gok[gi] ? u1 : ua[j];
           }
         }
       }
@@ -303,87 +123,104 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs a, int ny, int lpr_log2)
       }
     }
   }
-  if (shared || !next_routed(a, ny, &pos, &wk)) return;
- }
 }
 
-// down projection:  o[j][r] = Wd[r] . h_j   (fp32 out)
 template <int QF, int ACT, int NT, int GPL, int RPW>
-__global__ __launch_bounds__(256) void k_down(FfnArgs a, int ny, int lpr_log2) {
-  using CT = typename CodeOf<QF>::T;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd(ACT, NT, GPL)))) void k_gateup(
+    FfnArgs a, int ny, int lpr_log2) {
+  const bool shared = (int)blockIdx.y == ny;  // the extra last row of blocks
+  int pos = blockIdx.y;
+  Work wk;
+  if (shared) { wk.expert = -1; wk.lo = 0; wk.n = a.T; wk.pair0 = 0; }
+  else if (!next_routed(a, ny, &pos, &wk)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
+  const int rbase = (blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave)) * RPW * RPI;
+  for (;;) {
+    auto tok = [&](int jj) {
+      return shared ? jj : ((jj == 0 ? wk.pair0 : a.sorted_pairs[wk.lo + jj]) / a.K);
+    };
+    gateup_rows<QF, ACT, NT, GPL, RPW>(a, wk, shared, rbase, lane >> lpr_log2, lane & (LPR - 1), lpr_log2, tok);
+    if (shared || !next_routed(a, ny, &pos, &wk)) return;
+  }
+}
+
+// down projection:  o[j][r] = Wd[r] . h_j   (fp32 out); h rows of an expert are
+// contiguous in sorted order, so no index is loaded before the weights.
+template <int QF, int ACT, int NT, int GPL, int RPW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd(ACT, NT, GPL)))) void k_down(FfnArgs a, int ny,
+                                                                                    int lpr_log2) {
   const bool shared = (int)blockIdx.y == ny;
   int pos = blockIdx.y;
   Work wk;
   if (shared) { wk.expert = -1; wk.lo = 0; wk.n = a.T; }
   else if (!next_routed(a, ny, &pos, &wk)) return;
- for (;;) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
   const int sub = lane & (LPR - 1), rsub = lane >> lpr_log2;
   const int G = a.I / kGroup;
-  const MatView vd = expert_view<QF>(shared ? a.sdown : a.down, shared ? 0 : wk.expert, a.H, a.I);
+  const int rbase = (blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave)) * RPW * RPI;
+  const int r0 = rbase + rsub;
+  bool gok[GPL];
+#pragma unroll
+  for (int gi = 0; gi < GPL; ++gi) gok[gi] = sub + gi * LPR < G;
   const void* hin = shared ? a.hs : a.h;
   float* out = shared ? a.so : a.o;
-  const int r0 = (blockIdx.x * 4 + wave) * RPW * RPI + rsub;
-
-  for (int c0 = 0; c0 < wk.n; c0 += NT) {
-    const int nt = min(NT, wk.n - c0);
+  for (;;) {
     XGroup<QF, ACT> hg[NT][GPL];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      if (j < nt) {
-        const size_t row = shared ? (size_t)(c0 + j) : (size_t)(wk.lo + c0 + j);
-#pragma unroll
-        for (int gi = 0; gi < GPL; ++gi) {
-          const int g = sub + gi * LPR;
-          if (g < G) hg[j][gi].load(hin, row * a.I + (size_t)g * kGroup);
-        }
-      }
-    }
-    CT cd[RPW][GPL];
-    uint16_t sd[RPW][GPL], md[RPW][GPL];
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const int r = r0 + rr * RPI;
-#pragma unroll
-      for (int gi = 0; gi < GPL; ++gi) {
-        const int g = sub + gi * LPR;
-        if (r < a.H && g < G) {
-          cd[rr][gi] = *reinterpret_cast<const CT*>(vd.codes + (size_t)r * vd.row_bytes + (size_t)g * CodeOf<QF>::kBytes);
-          sd[rr][gi] = vd.scales[(size_t)r * G + g];
-          md[rr][gi] = (QF == MOE_Q2_ASYM_G32) ? vd.mins[(size_t)r * G + g] : (uint16_t)0;
-        }
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const int r = r0 + rr * RPI;
-      float acc[NT];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] = 0.f;
-#pragma unroll
-      for (int gi = 0; gi < GPL; ++gi) {
-        const int g = sub + gi * LPR;
-        if (r < a.H && g < G) {
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-            if (j < nt) acc[j] = group_acc<QF, ACT>(acc[j], cd[rr][gi], sd[rr][gi], md[rr][gi], hg[j][gi]);
-        }
-      }
+    auto load_h = [&](int c0) {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        if (j < nt) {
-          const float v = seg_sum(acc[j], LPR);
-          if (sub == 0 && r < a.H) {
-            const size_t row = shared ? (size_t)(c0 + j) : (size_t)(wk.lo + c0 + j);
-            out[row * a.H + r] = v;
+        const size_t row = (shared ? 0 : (size_t)wk.lo) + (size_t)(c0 + min(j, wk.n - 1 - c0));
+#pragma unroll
+        for (int gi = 0; gi < GPL; ++gi)
+          hg[j][gi].load_raw(hin, row * a.I + (size_t)min(sub + gi * LPR, G - 1) * kGroup);
+      }
+    };
+    load_h(0);
+    __builtin_amdgcn_sched_barrier(0);
+    const MatView vd = expert_view<QF>(shared ? a.sdown : a.down, shared ? 0 : wk.expert, a.H, a.I);
+    RowTile<QF, RPW, GPL> td;
+    td.load(vd, rbase, rsub, RPI, a.H, sub, LPR);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int c0 = 0; c0 < wk.n; c0 += NT) {
+      const int nt = min(NT, wk.n - c0);
+      if (c0 > 0) load_h(c0);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int gi = 0; gi < GPL; ++gi) hg[j][gi].prep();
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int r = r0 + rr * RPI;
+        float acc[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j] = 0.f;
+#pragma unroll
+        for (int gi = 0; gi < GPL; ++gi) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            if (j < nt) {
+              const float v1 = group_acc<QF, ACT>(acc[j], td.c[rr][gi], td.s[rr][gi], td.m[rr][gi], hg[j][gi]);
+              acc[j] = gok[gi] ? v1 : acc[j];
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          if (j < nt) {
+            const float v = seg_sum(acc[j], LPR);
+            if (sub == 0 && r < a.H) {
+              const size_t row = shared ? (size_t)(c0 + j) : (size_t)(wk.lo + c0 + j);
+              out[row * a.H + r] = v;
+            }
           }
         }
       }
     }
+    if (shared || !next_routed(a, ny, &pos, &wk)) return;
   }
-  if (shared || !next_routed(a, ny, &pos, &wk)) return;
- }
 }
 
 // lanes per row (power of two) and groups per lane for a row of `cols`
@@ -436,6 +273,213 @@ hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
 hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   return a.qfmt == MOE_Q4_SYM_G32 ? dispatch_act<MOE_Q4_SYM_G32>(a, false, s) : dispatch_act<MOE_Q2_ASYM_G32>(a, false, s);
+}
+
+
+// ============================================================================
+// Fused decode path (few tokens): the expert kernels compute the routing they
+// need themselves, so a layer is three kernels: router logits, gate/up, and
+// (one token) down projection with the weighted combine.
+
+constexpr int kFusedMaxPairs = 128;
+
+// gate/up with the top-K and the stable token -> expert ordering recomputed in
+// every block from the router logits (2 KiB per token at E = 512): block row y
+// is sorted position y and works only if it is its expert's first position.
+// The block at (0, 0) writes the routing outputs (ids, weights, offsets,
+// sorted_pairs, pair_pos) exactly as moe_router_topk and moe_permute do.
+template <int QF, int NT, int PL, int RPW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MOE_ACT_BF16, NT, 1)))) void
+k_fused_gateup(RouterArgs r, PermuteArgs pm, FfnArgs a, int lpr_log2) {
+  __shared__ int32_t s_ids[kFusedMaxPairs];
+  __shared__ int32_t s_pair[kFusedMaxPairs];
+  __shared__ int32_t s_exp[kFusedMaxPairs];
+  const int n = a.T * a.K;
+  const bool shared = (int)blockIdx.y == n;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  Work wk;
+  if (shared) {
+    wk.expert = -1; wk.lo = 0; wk.n = a.T; wk.pair0 = 0;
+  } else {
+    const bool lead = blockIdx.x == 0 && blockIdx.y == 0;
+    for (int t = wave; t < a.T; t += 4)
+      wave_topk_regs<PL>(r.logits + (size_t)t * r.E, r.E, r.K, lane, lead ? r.ids + (size_t)t * r.K : nullptr,
+                         lead ? r.wts + (size_t)t * r.K : nullptr, s_ids + t * r.K);
+    __syncthreads();
+    const int p = threadIdx.x;
+    if (p < n) {
+      const int e = s_ids[p];
+      int rank = 0;
+      for (int q = 0; q < n; ++q) {
+        const int eq = s_ids[q];
+        rank += (eq < e) | ((eq == e) & (q < p));
+      }
+      s_pair[rank] = p;
+      s_exp[rank] = e;
+      if (lead) {
+        pm.sorted_pairs[rank] = p;
+        pm.pair_pos[p] = rank;
+      }
+    }
+    __syncthreads();
+    if (lead) {
+      for (int e = threadIdx.x; e <= r.E; e += 256) {
+        int lo = 0, hi = n;  // first rank with expert >= e
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_exp[mid] < e) lo = mid + 1; else hi = mid;
+        }
+        pm.offsets[e] = lo;
+      }
+    }
+    const int y = blockIdx.y;
+    const int e = s_exp[y];
+    if (y > 0 && s_exp[y - 1] == e) return;  // not the expert's first position
+    int cnt = 1;
+    while (y + cnt < n && s_exp[y + cnt] == e) ++cnt;
+    wk.expert = e; wk.lo = y; wk.n = cnt; wk.pair0 = s_pair[y];
+  }
+  const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
+  const int rbase = (blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave)) * RPW * RPI;
+  auto tok = [&](int jj) { return shared ? jj : s_pair[wk.lo + jj] / a.K; };
+  gateup_rows<QF, MOE_ACT_BF16, NT, 1, RPW>(a, wk, shared, rbase, lane >> lpr_log2, lane & (LPR - 1), lpr_log2, tok);
+}
+
+// One token: down projection of the shared expert and the K selected experts
+// for the wave's rows, combined in slot order in registers:
+//   y[r] = o_shared[r] + sum_k w[k] o_k[r]   (the arithmetic of k_down + k_combine)
+// The K + 1 rows of h are staged in LDS once per block; the routing values are
+// read with scalar loads so they do not queue behind the vector loads.
+template <int QF, int KMAX, int RPW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_fused_down1(FfnArgs a,
+                                                                                             CombineArgs c,
+                                                                                             int lpr_log2) {
+  extern __shared__ uint4 s_h[];  // rows 0..K-1: h in sorted order; row K: the shared expert's h
+  const int K = a.K, I = a.I, row16 = I / 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
+  const int sub = lane & (LPR - 1), rsub = lane >> lpr_log2;
+  const int G = I / kGroup;
+  const int rbase = (blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave)) * RPW * RPI;
+  const bool has_shared = a.so != nullptr;  // the shared expert is present
+  // 1. routing of the token (uniform scalar loads) and every slot's weight rows
+  int pos[KMAX];
+  float wgt[KMAX];
+  RowTile<QF, RPW, 1> tw[KMAX + 1];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int kk = min(k, K - 1);  // clamped: duplicates past K are loaded but unused
+    const int e = __builtin_amdgcn_readfirstlane(a.ids[kk]);
+    pos[k] = __builtin_amdgcn_readfirstlane(c.pair_pos[kk]);
+    wgt[k] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.w[kk])));
+    tw[k].load(expert_view<QF>(a.down, e, a.H, I), rbase, rsub, RPI, a.H, sub, LPR);
+  }
+  if (has_shared) tw[KMAX].load(expert_view<QF>(a.sdown, 0, a.H, I), rbase, rsub, RPI, a.H, sub, LPR);
+  // 2. the h rows into LDS, in rounds of kStage 16-byte chunks per thread
+  constexpr int kStage = 5;
+  const int n16 = (K + (has_shared ? 1 : 0)) * row16;
+  for (int base = 0; base < n16; base += 256 * kStage) {
+    uint4 st[kStage];
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const int idx = min(base + (int)threadIdx.x + i * 256, n16 - 1);
+      const int slot = idx / row16, off = idx % row16;
+      const uint16_t* src = slot < K ? reinterpret_cast<const uint16_t*>(a.h) + (size_t)slot * I
+                                     : reinterpret_cast<const uint16_t*>(a.hs);
+      st[i] = reinterpret_cast<const uint4*>(src)[off];
+    }
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const int idx = base + (int)threadIdx.x + i * 256;
+      if (idx < n16) s_h[idx] = st[i];
+    }
+  }
+  __syncthreads();
+  const bool gok = sub < G;
+  const int gc = min(sub, G - 1);
+  auto slot_out = [&](const RowTile<QF, RPW, 1>& t, int hrow, int rr) {
+    XGroup<QF, MOE_ACT_BF16> hg;
+    const uint4* src = s_h + (size_t)hrow * row16 + gc * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hg.q[i] = src[i];
+    hg.prep();
+    const float v = group_acc<QF, MOE_ACT_BF16>(0.f, t.c[rr][0], t.s[rr][0], t.m[rr][0], hg);
+    return seg_sum(gok ? v : 0.f, LPR);
+  };
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int r = rbase + rsub + rr * RPI;
+    float acc = has_shared ? slot_out(tw[KMAX], K, rr) : 0.f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (k < K) acc = fmaf(wgt[k], slot_out(tw[k], pos[k], rr), acc);
+    if (sub == 0 && r < a.H) {
+      c.y[r] = acc;
+      if (c.x_next) store_act<MOE_ACT_BF16>(c.x_next, r, load_act<MOE_ACT_BF16>(c.x_resid, r) + acc);
+    }
+  }
+}
+
+bool fused_decode_ok(int T, int K, int E, int H, int I, int act) {
+  return act == MOE_ACT_BF16 && T * K <= kFusedMaxPairs && K <= 64 && E <= 64 * kRegLogits && H <= 64 * kGroup &&
+         I <= 64 * kGroup;
+}
+
+bool fused_down1_ok(int T, int K, int I) { return T == 1 && K <= 16 && I <= 2048 && (K + 1) * I * 2 <= 65536; }
+
+template <int QF>
+static hipError_t fused_gateup_pl(const RouterArgs& r, const PermuteArgs& pm, const FfnArgs& a, hipStream_t s) {
+  int lpr_log2, gpl;
+  lane_split(a.H, &lpr_log2, &gpl);
+  const int rpi = 64 >> lpr_log2;
+  const int rows_per_block = 4 * kRPW * rpi;
+  const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, a.T * a.K + (a.n_shared && a.hs ? 1 : 0));
+  const int pl = regs_per_lane(a.E);
+  auto go = [&](auto kern) { kern<<<grid, 256, 0, s>>>(r, pm, a, lpr_log2); };
+  if (a.T == 1) {
+    switch (pl) {
+      case 1: go(k_fused_gateup<QF, 1, 1, kRPW>); break;
+      case 2: go(k_fused_gateup<QF, 1, 2, kRPW>); break;
+      case 4: go(k_fused_gateup<QF, 1, 4, kRPW>); break;
+      case 8: go(k_fused_gateup<QF, 1, 8, kRPW>); break;
+      default: go(k_fused_gateup<QF, 1, 16, kRPW>); break;
+    }
+  } else {
+    switch (pl) {
+      case 1: go(k_fused_gateup<QF, 4, 1, kRPW>); break;
+      case 2: go(k_fused_gateup<QF, 4, 2, kRPW>); break;
+      case 4: go(k_fused_gateup<QF, 4, 4, kRPW>); break;
+      case 8: go(k_fused_gateup<QF, 4, 8, kRPW>); break;
+      default: go(k_fused_gateup<QF, 4, 16, kRPW>); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_gateup(const RouterArgs& r, const PermuteArgs& pm, const FfnArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  return a.qfmt == MOE_Q4_SYM_G32 ? fused_gateup_pl<MOE_Q4_SYM_G32>(r, pm, a, s)
+                                  : fused_gateup_pl<MOE_Q2_ASYM_G32>(r, pm, a, s);
+}
+
+template <int QF>
+static hipError_t fused_down1_q(const FfnArgs& a, const CombineArgs& c, hipStream_t s) {
+  int lpr_log2, gpl;
+  lane_split(a.I, &lpr_log2, &gpl);
+  const int rpi = 64 >> lpr_log2;
+  constexpr int kRpwDown = 1;
+  const int rows_per_block = 4 * kRpwDown * rpi;
+  const dim3 grid((a.H + rows_per_block - 1) / rows_per_block);
+  const size_t lds = (size_t)(a.K + 1) * a.I * 2;
+  if (a.K <= 4) k_fused_down1<QF, 4, kRpwDown><<<grid, 256, lds, s>>>(a, c, lpr_log2);
+  else if (a.K <= 8) k_fused_down1<QF, 8, kRpwDown><<<grid, 256, lds, s>>>(a, c, lpr_log2);
+  else if (a.K <= 12) k_fused_down1<QF, 12, kRpwDown><<<grid, 256, lds, s>>>(a, c, lpr_log2);
+  else k_fused_down1<QF, 16, kRpwDown><<<grid, 256, lds, s>>>(a, c, lpr_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_down1(const FfnArgs& a, const CombineArgs& c, hipStream_t s) {
+  return a.qfmt == MOE_Q4_SYM_G32 ? fused_down1_q<MOE_Q4_SYM_G32>(a, c, s) : fused_down1_q<MOE_Q2_ASYM_G32>(a, c, s);
 }
 
 }  // namespace moe

@@ -1,0 +1,234 @@
+// Dequantising dot products of packed group-32 rows with bf16 / fp32
+// activations, shared by the expert kernels (wave64, gfx950).
+//
+// Inner product of one group (bf16 activations): each code u becomes the exact
+// bf16 number 128 + u by OR-ing it into the mantissa of 0x4300 (=128), two
+// codes per 32-bit word, and v_dot2_f32_bf16 multiplies the pair with a pair
+// of activations in fp32 (products of an 8-bit code and a bf16 value are exact
+// in fp32).  The offset is removed with a per-group constant computed once per
+// token:  sum (u - 8) x = sum (128 + u) x - 136 sum x   (4-bit),
+//         sum u x       = sum (128 + u) x - 128 sum x   (2-bit),
+// and the group scale (and 2-bit minimum) is applied once per group:
+//         acc += s * sum(q x)            (4-bit, w = s q)
+//         acc += s * sum(u x) + m sum x  (2-bit, w = s u + m).
+// Activation pairs are pre-arranged per token to match the code pairs a mask
+// and a shift produce: 4-bit word i of a group yields pairs (8i+j, 8i+4+j) for
+// j = 0..3 from nibbles j and j+4; 2-bit word i yields pairs (16i+j, 16i+8+j)
+// for j = 0..7 from crumbs j and j+8.
+#pragma once
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int QF> struct CodeOf;
+template <> struct CodeOf<MOE_Q4_SYM_G32> { using T = u32x4; static constexpr int kBytes = 16; };
+template <> struct CodeOf<MOE_Q2_ASYM_G32> { using T = u32x2; static constexpr int kBytes = 8; };
+
+// Prepared activations of one 32-element group of one token.
+template <int QF, int ACT> struct XGroup;
+
+template <int QF> struct XGroup<QF, MOE_ACT_BF16> {
+  uint4 q[4];      // the group's 32 raw bf16 values
+  uint32_t p[16];  // bf16 pairs matching the code pairs
+  float c;         // 136 * sum x (4-bit) or 128 * sum x (2-bit)
+  float sx;        // sum x (2-bit only)
+
+  __device__ __forceinline__ void load_raw(const void* base, size_t elem) {
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = src[i];
+  }
+  __device__ __forceinline__ void prep() {
+    if constexpr (QF == MOE_Q4_SYM_G32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // elements 8i..8i+7 in q[i]
+        p[4 * i + 0] = (q[i].x & 0xffffu) | (q[i].z << 16);
+        p[4 * i + 1] = (q[i].x >> 16) | (q[i].z & 0xffff0000u);
+        p[4 * i + 2] = (q[i].y & 0xffffu) | (q[i].w << 16);
+        p[4 * i + 3] = (q[i].y >> 16) | (q[i].w & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {  // elements 16i..16i+7 in q[2i], 16i+8..16i+15 in q[2i+1]
+        const uint32_t a[4] = {q[2 * i].x, q[2 * i].y, q[2 * i].z, q[2 * i].w};
+        const uint32_t b[4] = {q[2 * i + 1].x, q[2 * i + 1].y, q[2 * i + 1].z, q[2 * i + 1].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          p[8 * i + 2 * m] = (a[m] & 0xffffu) | (b[m] << 16);
+          p[8 * i + 2 * m + 1] = (a[m] >> 16) | (b[m] & 0xffff0000u);
+        }
+      }
+    }
+    constexpr uint32_t kOff = (QF == MOE_Q4_SYM_G32) ? 0x43084308u : 0x43004300u;  // (136,136) / (128,128)
+    float c0 = 0.f, c1 = 0.f, s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      c0 = dot2_bf16(kOff, p[i], c0);
+      c1 = dot2_bf16(kOff, p[i + 1], c1);
+      if constexpr (QF == MOE_Q2_ASYM_G32) {
+        s0 = dot2_bf16(0x3f803f80u, p[i], s0);
+        s1 = dot2_bf16(0x3f803f80u, p[i + 1], s1);
+      }
+    }
+    c = c0 + c1;
+    sx = s0 + s1;
+  }
+};
+
+template <int QF> struct XGroup<QF, MOE_ACT_F32> {
+  float4 r[8];  // the group's 32 fp32 values
+  float sx;
+  __device__ __forceinline__ void load_raw(const void* base, size_t elem) {
+    const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = src[i];
+  }
+  __device__ __forceinline__ void prep() {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += (r[i].x + r[i].y) + (r[i].z + r[i].w);
+    sx = s;
+  }
+  __device__ __forceinline__ float at(int k) const {
+    const float4 f = r[k >> 2];
+    return (k & 3) == 0 ? f.x : (k & 3) == 1 ? f.y : (k & 3) == 2 ? f.z : f.w;
+  }
+};
+
+// (a & m) | c in one instruction (the compiler otherwise emits an AND and an
+// OR, since these constants need a literal and VOP3 takes none on gfx9; here
+// the mask sits in a scalar register and the constant in a vector one: one
+// scalar operand per instruction on gfx9).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
+  return d;
+}
+
+// sum over the group of q*x (4-bit, q = u - 8) or u*x (2-bit).
+template <int QF, int ACT>
+__device__ __forceinline__ float group_dot(const typename CodeOf<QF>::T& cw, const XGroup<QF, ACT>& x) {
+  if constexpr (ACT == MOE_ACT_BF16) {
+    float d0 = 0.f, d1 = 0.f;
+    if constexpr (QF == MOE_Q4_SYM_G32) {
+      uint32_t w[4] = {cw[0], cw[1], cw[2], cw[3]};
+      // unpack at the point of use (an empty asm that "updates" the words keeps
+      // the compiler from hoisting every row's shifted copies at once)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(w[i]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        d0 = dot2_bf16(and_or(w[i], 0x000f000fu, 0x43004300u), x.p[4 * i + 0], d0);
+        d1 = dot2_bf16(and_or(w[i] >> 4, 0x000f000fu, 0x43004300u), x.p[4 * i + 1], d1);
+        d0 = dot2_bf16(and_or(w[i] >> 8, 0x000f000fu, 0x43004300u), x.p[4 * i + 2], d0);
+        d1 = dot2_bf16(and_or(w[i] >> 12, 0x000f000fu, 0x43004300u), x.p[4 * i + 3], d1);
+      }
+    } else {
+      uint32_t w[2] = {cw[0], cw[1]};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(w[i]));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          d0 = dot2_bf16(and_or(w[i] >> (2 * j), 0x00030003u, 0x43004300u), x.p[8 * i + j], d0);
+          d1 = dot2_bf16(and_or(w[i] >> (2 * j + 2), 0x00030003u, 0x43004300u), x.p[8 * i + j + 1], d1);
+        }
+      }
+    }
+    return (d0 + d1) - x.c;
+  } else {
+    float d0 = 0.f, d1 = 0.f;
+    if constexpr (QF == MOE_Q4_SYM_G32) {
+      const uint32_t w[4] = {cw[0], cw[1], cw[2], cw[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          d0 = fmaf((float)((int)((w[i] >> (4 * j)) & 15u) - 8), x.at(8 * i + j), d0);
+          d1 = fmaf((float)((int)((w[i] >> (4 * j + 4)) & 15u) - 8), x.at(8 * i + j + 1), d1);
+        }
+      }
+    } else {
+      const uint32_t w[2] = {cw[0], cw[1]};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          d0 = fmaf((float)((w[i] >> (2 * j)) & 3u), x.at(16 * i + j), d0);
+          d1 = fmaf((float)((w[i] >> (2 * j + 2)) & 3u), x.at(16 * i + j + 1), d1);
+        }
+      }
+    }
+    return d0 + d1;
+  }
+}
+
+template <int QF, int ACT>
+__device__ __forceinline__ float group_acc(float acc, const typename CodeOf<QF>::T& cw, uint16_t s16, uint16_t m16,
+                                           const XGroup<QF, ACT>& x) {
+  const float d = group_dot<QF, ACT>(cw, x);
+  acc = fmaf(f16_to_f32(s16), d, acc);
+  if constexpr (QF == MOE_Q2_ASYM_G32) acc = fmaf(f16_to_f32(m16), x.sx, acc);
+  return acc;
+}
+
+struct MatView {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* mins;
+  size_t row_bytes;  // code bytes per row
+  int groups;        // groups per row
+};
+
+template <int QF>
+__device__ __forceinline__ MatView expert_view(const QMat& m, int e, int rows, int cols) {
+  MatView v;
+  v.row_bytes = (size_t)cols * (QF == MOE_Q4_SYM_G32 ? 4 : 2) / 8;
+  v.groups = cols / kGroup;
+  v.codes = m.codes + (size_t)e * rows * v.row_bytes;
+  v.scales = m.scales + (size_t)e * rows * v.groups;
+  v.mins = m.mins ? m.mins + (size_t)e * rows * v.groups : nullptr;
+  return v;
+}
+
+// Packed codes, scales (and minima) of RPW rows x GPL groups for one lane.
+template <int QF, int RPW, int GPL>
+struct RowTile {
+  using CT = typename CodeOf<QF>::T;
+  CT c[RPW][GPL];
+  uint16_t s[RPW][GPL];
+  uint16_t m[RPW][GPL];
+
+  // Branch-free: out-of-range rows / groups load a clamped in-range address
+  // (their results are dropped later), so that no load sits in a conditional
+  // block and all of them are in flight together.  Addresses are a
+  // wave-uniform row base plus a 32-bit lane offset (scalar-base loads).
+  // rbase: first row of the wave (uniform); the lane's row is rbase + rsub +
+  // rr * rpi.
+  __device__ __forceinline__ void load(const MatView& v, int rbase, int rsub, int rpi, int rows, int sub, int lpr) {
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int ru = min(rbase + rr * rpi, rows - 1);          // uniform
+      const int rc = min(ru + rsub, rows - 1);                 // this lane's row, >= ru
+      const uint8_t* cb = v.codes + (size_t)ru * v.row_bytes;  // uniform bases
+      const uint16_t* sb = v.scales + (size_t)ru * v.groups;
+#pragma unroll
+      for (int gi = 0; gi < GPL; ++gi) {
+        const int gc = min(sub + gi * lpr, v.groups - 1);
+        const uint32_t co = (uint32_t)(rc - ru) * (uint32_t)v.row_bytes + (uint32_t)gc * CodeOf<QF>::kBytes;
+        const uint32_t so = (uint32_t)(rc - ru) * (uint32_t)v.groups + (uint32_t)gc;
+        c[rr][gi] = __builtin_nontemporal_load(reinterpret_cast<const CT*>(cb + co));
+        s[rr][gi] = sb[so];
+        m[rr][gi] = (QF == MOE_Q2_ASYM_G32) ? (v.mins + (size_t)ru * v.groups)[so] : (uint16_t)0;
+      }
+    }
+  }
+};
+
+}  // namespace moe

@@ -109,14 +109,14 @@ RouterArgs router_args(const moe_layer& L, const void* x, int32_t T, float* logi
 
 // The shared expert runs only if the layer has one and its output (hs for
 // gate/up, so for down) is given.
-FfnArgs ffn_args(const moe_layer& L, const void* x, int32_t T, const int32_t* offsets, const int32_t* sorted,
-                 void* h, void* hs, float* o, float* so) {
+FfnArgs ffn_args(const moe_layer& L, const void* x, int32_t T, const int32_t* ids, const int32_t* offsets,
+                 const int32_t* sorted, void* h, void* hs, float* o, float* so) {
   FfnArgs f{};
   f.gate = qmat(L.routed.gate); f.up = qmat(L.routed.up); f.down = qmat(L.routed.down);
   if (L.shared.n == 1) { f.sgate = qmat(L.shared.gate); f.sup = qmat(L.shared.up); f.sdown = qmat(L.shared.down); }
   f.n_shared = L.shared.n == 1 ? 1 : 0;
   f.T = T; f.H = L.hidden; f.I = L.inter; f.E = L.n_experts; f.K = L.top_k; f.qfmt = L.qfmt; f.act = L.act;
-  f.x = x; f.offsets = offsets; f.sorted_pairs = sorted;
+  f.x = x; f.ids = ids; f.offsets = offsets; f.sorted_pairs = sorted;
   f.h = h; f.hs = f.n_shared ? hs : nullptr; f.o = o; f.so = f.n_shared ? so : nullptr;
   return f;
 }
@@ -127,16 +127,27 @@ moe_status layer_forward_impl(const moe_layer& L, const void* x, int32_t T, floa
   int32_t* ids = ids_opt ? ids_opt : at<int32_t>(ws, W.ids);
   float* wts = w_opt ? w_opt : at<float>(ws, W.w);
   const RouterArgs ra = router_args(L, x, T, at<float>(ws, W.logits), ids, wts);
-  MOE_TRY(dev(launch_router_logits(ra, s)));
-  MOE_TRY(dev(launch_topk(ra, s)));
   PermuteArgs pa{ids, at<int32_t>(ws, W.offsets), at<int32_t>(ws, W.sorted), at<int32_t>(ws, W.pos),
                  at<int32_t>(ws, W.chunk), T, L.top_k, L.n_experts};
-  MOE_TRY(dev(launch_permute(pa, s)));
-  const FfnArgs fa = ffn_args(L, x, T, pa.offsets, pa.sorted_pairs, at<void>(ws, W.h), at<void>(ws, W.hs),
+  const FfnArgs fa = ffn_args(L, x, T, ids, pa.offsets, pa.sorted_pairs, at<void>(ws, W.h), at<void>(ws, W.hs),
                               at<float>(ws, W.o), at<float>(ws, W.so));
+  const CombineArgs ca{fa.o, fa.so, pa.pair_pos, wts, x_next ? x : nullptr, x_next, y, T, L.hidden, L.top_k, L.act};
+  MOE_TRY(dev(launch_router_logits(ra, s)));
+  if (fused_decode_ok(T, L.top_k, L.n_experts, L.hidden, L.inter, L.act)) {
+    // few tokens: routing recomputed inside the gate/up kernel; one token: down + combine fused
+    MOE_TRY(dev(launch_fused_gateup(ra, pa, fa, s)));
+    if (fused_down1_ok(T, L.top_k, L.inter)) return dev(launch_fused_down1(fa, ca, s));
+    MOE_TRY(dev(launch_down(fa, s)));
+    return dev(launch_combine(ca, s));
+  }
+  if (route_small_ok(T, L.top_k, L.n_experts)) {
+    MOE_TRY(dev(launch_route_small(ra, pa, s)));
+  } else {
+    MOE_TRY(dev(launch_topk(ra, s)));
+    MOE_TRY(dev(launch_permute(pa, s)));
+  }
   MOE_TRY(dev(launch_gateup(fa, s)));
   MOE_TRY(dev(launch_down(fa, s)));
-  const CombineArgs ca{fa.o, fa.so, pa.pair_pos, wts, x_next ? x : nullptr, x_next, y, T, L.hidden, L.top_k, L.act};
   return dev(launch_combine(ca, s));
 }
 
@@ -192,13 +203,15 @@ moe_status moe_permute(const moe_layer* layer, const int32_t* topk_ids, int32_t 
   return dev(launch_permute(pa, s));  // T == 0 still writes the all-zero offsets
 }
 
-moe_status moe_expert_ffn_q(const moe_layer* layer, const void* x, int32_t T, const int32_t* expert_offsets,
-                            const int32_t* sorted_pairs, float* expert_out, float* shared_out_opt, void* h_opt,
-                            void* shared_h_opt, void* ws, size_t ws_bytes, void* stream) {
+moe_status moe_expert_ffn_q(const moe_layer* layer, const void* x, int32_t T, const int32_t* topk_ids,
+                            const int32_t* expert_offsets, const int32_t* sorted_pairs, float* expert_out,
+                            float* shared_out_opt, void* h_opt, void* shared_h_opt, void* ws, size_t ws_bytes,
+                            void* stream) {
   MOE_TRY(check_layer(layer));
   MOE_TRY(check_tokens(layer, T));
   if (T == 0) return MOE_OK;
-  if (!x || !expert_offsets || !sorted_pairs || !expert_out || !aligned(x, 16) || !aligned(expert_out, 16))
+  if (!x || !topk_ids || !expert_offsets || !sorted_pairs || !expert_out || !aligned(x, 16) ||
+      !aligned(expert_out, 16))
     return MOE_E_ARG;
   if ((h_opt && !aligned(h_opt, 16)) || (shared_h_opt && !aligned(shared_h_opt, 16))) return MOE_E_ARG;
   if (shared_out_opt && !aligned(shared_out_opt, 16)) return MOE_E_ARG;
@@ -211,38 +224,42 @@ moe_status moe_expert_ffn_q(const moe_layer* layer, const void* x, int32_t T, co
     if (!hs) hs = at<void>(ws, W.hs);
   }
   const bool shared = layer->shared.n == 1 && shared_out_opt != nullptr;
-  const FfnArgs fa = ffn_args(*layer, x, T, expert_offsets, sorted_pairs, h, shared ? hs : nullptr, expert_out,
-                              shared ? shared_out_opt : nullptr);
+  const FfnArgs fa = ffn_args(*layer, x, T, topk_ids, expert_offsets, sorted_pairs, h, shared ? hs : nullptr,
+                              expert_out, shared ? shared_out_opt : nullptr);
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   MOE_TRY(dev(launch_gateup(fa, s)));
   return dev(launch_down(fa, s));
 }
 
-moe_status moe_expert_gate_up_q(const moe_layer* layer, const void* x, int32_t T, const int32_t* expert_offsets,
-                                const int32_t* sorted_pairs, void* h, void* shared_h_opt, void* stream) {
+moe_status moe_expert_gate_up_q(const moe_layer* layer, const void* x, int32_t T, const int32_t* topk_ids,
+                                const int32_t* expert_offsets, const int32_t* sorted_pairs, void* h,
+                                void* shared_h_opt, void* stream) {
   MOE_TRY(check_layer(layer));
   MOE_TRY(check_tokens(layer, T));
   if (T == 0) return MOE_OK;
-  if (!x || !expert_offsets || !sorted_pairs || !h || !aligned(x, 16) || !aligned(h, 16)) return MOE_E_ARG;
+  if (!x || !topk_ids || !expert_offsets || !sorted_pairs || !h || !aligned(x, 16) || !aligned(h, 16))
+    return MOE_E_ARG;
   if (shared_h_opt && !aligned(shared_h_opt, 16)) return MOE_E_ARG;
   const bool shared = layer->shared.n == 1 && shared_h_opt != nullptr;
-  const FfnArgs fa = ffn_args(*layer, x, T, expert_offsets, sorted_pairs, h, shared ? shared_h_opt : nullptr,
-                              nullptr, nullptr);
+  const FfnArgs fa = ffn_args(*layer, x, T, topk_ids, expert_offsets, sorted_pairs, h,
+                              shared ? shared_h_opt : nullptr, nullptr, nullptr);
   return dev(launch_gateup(fa, reinterpret_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_expert_down_q(const moe_layer* layer, const void* h, const void* shared_h_opt, int32_t T,
-                             const int32_t* expert_offsets, float* expert_out, float* shared_out_opt,
-                             void* stream) {
+                             const int32_t* topk_ids, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                             float* expert_out, float* shared_out_opt, void* stream) {
   MOE_TRY(check_layer(layer));
   MOE_TRY(check_tokens(layer, T));
   if (T == 0) return MOE_OK;
-  if (!h || !expert_offsets || !expert_out || !aligned(h, 16) || !aligned(expert_out, 16)) return MOE_E_ARG;
+  if (!h || !topk_ids || !expert_offsets || !sorted_pairs || !expert_out || !aligned(h, 16) ||
+      !aligned(expert_out, 16))
+    return MOE_E_ARG;
   if ((shared_h_opt && !aligned(shared_h_opt, 16)) || (shared_out_opt && !aligned(shared_out_opt, 16)))
     return MOE_E_ARG;
   if (shared_out_opt && layer->shared.n == 1 && !shared_h_opt) return MOE_E_ARG;
   const bool shared = layer->shared.n == 1 && shared_out_opt != nullptr;
-  FfnArgs fa = ffn_args(*layer, nullptr, T, expert_offsets, nullptr, const_cast<void*>(h),
+  FfnArgs fa = ffn_args(*layer, nullptr, T, topk_ids, expert_offsets, sorted_pairs, const_cast<void*>(h),
                         shared ? const_cast<void*>(shared_h_opt) : nullptr, expert_out,
                         shared ? shared_out_opt : nullptr);
   return dev(launch_down(fa, reinterpret_cast<hipStream_t>(stream)));

@@ -43,6 +43,9 @@ struct PermuteArgs {
 };
 size_t permute_scratch_ints(int T, int K, int E);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// top-K and permutation in one block for small batches (T*K <= 256, E <= 1024)
+bool route_small_ok(int T, int K, int E);
+hipError_t launch_route_small(const RouterArgs& a, const PermuteArgs& p, hipStream_t s);
 
 // ---------------------------------------------------------------- expert FFN
 struct FfnArgs {
@@ -51,6 +54,7 @@ struct FfnArgs {
   int n_shared;
   int T, H, I, E, K, qfmt, act;
   const void* x;               // [T][H] act
+  const int32_t* ids;          // [T*K] expert of each pair
   const int32_t* offsets;      // [E+1]
   const int32_t* sorted_pairs; // [T*K]
   void* h;                     // [T*K][I] act, sorted order
@@ -73,6 +77,15 @@ struct CombineArgs {
   int T, H, K, act;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- fused decode path
+// gate/up with the routing (top-K, permutation) recomputed per block: T*K <= 128,
+// K <= 64, E <= 1024, H, I <= 2048, bf16 activations
+bool fused_decode_ok(int T, int K, int E, int H, int I, int act);
+hipError_t launch_fused_gateup(const RouterArgs& r, const PermuteArgs& pm, const FfnArgs& a, hipStream_t s);
+// one token: down projection fused with the combine (K <= 16, I <= 2048)
+bool fused_down1_ok(int T, int K, int I);
+hipError_t launch_fused_down1(const FfnArgs& a, const CombineArgs& c, hipStream_t s);
 
 // ---------------------------------------------------------------- test hook
 hipError_t launch_dequant(const QMat& m, int qfmt, int rows, int cols, float* out, hipStream_t s);

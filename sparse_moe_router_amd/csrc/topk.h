@@ -1,0 +1,104 @@
+// Top-K selection of router logits by one wave (wave64, gfx950): keys, the
+// register-resident selection and its renormalised softmax weights.
+#pragma once
+
+#include "moe_device.h"
+
+namespace moe {
+
+constexpr int kRegLogits = 16;  // logits per lane held in registers: E <= 1024
+
+// Order-preserving map of a float to uint32 (NaN treated as -inf); every real
+// value maps to >= 0x007fffff, so 0 marks "taken / empty".
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f != f) f = -INFINITY;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// 64-bit selection key: larger logit first, then smaller expert id.
+__device__ __forceinline__ uint64_t sel_key(float l, int e) {
+  return ((uint64_t)order_key(l) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+__device__ __forceinline__ int key_id(uint64_t k) { return (int)(0xffffffffu - (uint32_t)k); }
+
+// Top-K of one token by one wave with the token's logits in registers
+// (expert e = lane + 64 i, PL per lane).  Each lane keeps its best remaining
+// candidate (largest key, lowest id on equal keys); a round takes the wave
+// maximum of the 32-bit keys (one DPP max per step), the owner of the winner
+// (the lowest id among lanes tied at the maximum) drops it and rescans.
+// Writes ids and the renormalised softmax weights of the K selected logits
+// (unless ids is null; then only lds_ids, which requires K <= 64).
+template <int PL>
+__device__ __forceinline__ void wave_topk_regs(const float* lg, int E, int K, int lane, int32_t* ids, float* wts,
+                                               int32_t* lds_ids) {
+  float v[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) v[i] = lg[min(lane + 64 * i, E - 1)];  // clamped: no conditional loads
+  uint32_t key[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) key[i] = (lane + 64 * i < E) ? order_key(v[i]) : 0u;
+  // the lane's best: scanning i upward with a strict '>' keeps the lowest id on ties
+  auto rescan = [&](uint32_t* bk, int* bid) {
+    *bk = 0u; *bid = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const bool better = key[i] > *bk;
+      *bid = better ? lane + 64 * i : *bid;
+      *bk = better ? key[i] : *bk;
+    }
+  };
+  uint32_t bk;
+  int bid;
+  rescan(&bk, &bid);
+  uint32_t mine = 0;   // lane k keeps the key and id picked in round k (k < 64)
+  int mine_id = 0;
+  uint32_t top = 0;
+  for (int k = 0; k < K; ++k) {
+    const uint32_t m = wave_max_u32(bk);
+    const uint64_t tied = __ballot(bk == m);
+    int id;
+    if (__popcll(tied) == 1) {
+      id = __builtin_amdgcn_readlane(bid, (int)__ffsll((unsigned long long)tied) - 1);
+    } else {  // several lanes hold an equal key: the lowest id wins
+      id = wave_min_i32(bk == m ? bid : 0x7fffffff);
+    }
+    if (k == 0) top = m;
+    if (lane == (k & 63)) { mine = m; mine_id = id; }
+    if (K > 64 && ids && lane == 0) ids[k] = id;
+    if (lds_ids && lane == 0) lds_ids[k] = id;
+    if ((id & 63) == lane) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) key[i] = (lane + 64 * i == id) ? 0u : key[i];
+      rescan(&bk, &bid);
+    }
+  }
+  const float l0 = key_value(top);
+  if (K <= 64) {
+    const float ex = lane < K ? expf(key_value(mine) - l0) : 0.f;
+    const float total = wave_sum(ex);
+    if (lane < K && ids) {  // ids / wts may be null: selection into LDS only
+      ids[lane] = mine_id;
+      wts[lane] = ex / total;
+    }
+  } else {  // rare: more than 64 slots, weights from the stored logits
+    __builtin_amdgcn_s_waitcnt(0);
+    float part = 0.f;
+    for (int k = lane; k < K; k += 64) part += expf(lg[ids[k]] - l0);
+    const float total = wave_sum(part);
+    for (int k = lane; k < K; k += 64) wts[k] = expf(lg[ids[k]] - l0) / total;
+  }
+}
+
+// logits per lane held in registers for E experts: 1, 2, 4, 8 or 16
+inline int regs_per_lane(int E) {
+  int pl = 1;
+  while (64 * pl < E) pl <<= 1;
+  return pl;
+}
+
+}  // namespace moe

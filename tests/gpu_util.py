@@ -45,7 +45,7 @@ def run_steps(L: api.Layer, x: torch.Tensor, T: int, with_shared=True):
     so = torch.empty((T, H), dtype=torch.float32, device=dev) if with_shared else None
     hh = torch.empty((T * K, L.inter), dtype=L.act_dtype, device=dev)
     hs = torch.empty((T, L.inter), dtype=L.act_dtype, device=dev) if with_shared else None
-    api.moe_expert_ffn_q(L, x, T, off, sp, o, so, hh, hs, ws)
+    api.moe_expert_ffn_q(L, x, T, ids, off, sp, o, so, hh, hs, ws)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     api.moe_combine(L, o, so, pp, w, T, y)
     torch.cuda.synchronize()

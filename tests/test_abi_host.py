@@ -92,7 +92,7 @@ def test_token_count_rules():
     # T == 0 is a no-op that needs no buffers at all
     assert lib.moe_layer_forward(r, None, 0, None, None, None, None, None, 0, None) == api.MOE_OK
     assert lib.moe_router_topk(r, None, 0, None, None, None, None, 0, None) == api.MOE_OK
-    assert lib.moe_expert_ffn_q(r, None, 0, None, None, None, None, None, None, None, 0, None) == api.MOE_OK
+    assert lib.moe_expert_ffn_q(r, None, 0, None, None, None, None, None, None, None, None, 0, None) == api.MOE_OK
     assert lib.moe_combine(r, None, None, None, None, 0, None, None, None, None) == api.MOE_OK
 
 

@@ -136,6 +136,11 @@ CASES = [
     (224, 352, 30, 6, 33, "q2_asym_g32", "f32", True),
     (128, 64, 64, 8, 600, "q4_sym_g32", "bf16", True),       # 4800 pairs: multi-block permutation
     (128, 64, 300, 7, 700, "q2_asym_g32", "bf16", True),
+    (96, 160, 13, 3, 1, "q4_sym_g32", "bf16", True),          # one token: fused down + combine
+    (64, 96, 8, 8, 1, "q2_asym_g32", "bf16", False),
+    (128, 1024, 20, 16, 1, "q4_sym_g32", "bf16", True),       # K = 16 slots, I = 1024
+    (64, 64, 1500, 3, 4, "q4_sym_g32", "bf16", True),         # E > 1024: top-k from LDS
+    (96, 64, 1024, 70, 3, "q2_asym_g32", "bf16", True),       # K > 64 slots per token
 ]
 
 
@@ -149,8 +154,9 @@ def test_small_layers(case):
     full_check(ld, x, strict=i >= 256)
 
 
-def test_no_shared_expert():
-    spec = synth.LayerSpec("noshared", 64, 8, 3, 96, 6, "q4_sym_g32", "bf16", 0.3, 1.1, family=61, n_shared=0)
+@pytest.mark.parametrize("t", [1, 6])
+def test_no_shared_expert(t):
+    spec = synth.LayerSpec("noshared", 64, 8, 3, 96, t, "q4_sym_g32", "bf16", 0.3, 1.1, family=61, n_shared=0)
     ld = synth.gen_layer(spec)
     x = synth.gen_x(spec)
     L = gu.device_layer(ld)
@@ -331,13 +337,13 @@ def test_split_expert_calls_match_ffn():
     g = gu.run_steps(L, xd, 7)
     dev = gu.DEV
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    off, sp = t(g["offsets"]), t(g["sorted_pairs"])
+    off, sp, ids = t(g["offsets"]), t(g["sorted_pairs"]), t(g["ids"].astype(np.int32))
     h = torch.empty((42, 768), dtype=torch.bfloat16, device=dev)
     hs = torch.empty((7, 768), dtype=torch.bfloat16, device=dev)
-    api.moe_expert_gate_up_q(L, xd, 7, off, sp, h, hs)
+    api.moe_expert_gate_up_q(L, xd, 7, ids, off, sp, h, hs)
     o = torch.empty((42, 2048), dtype=torch.float32, device=dev)
     so = torch.empty((7, 2048), dtype=torch.float32, device=dev)
-    api.moe_expert_down_q(L, h, hs, 7, off, o, so)
+    api.moe_expert_down_q(L, h, hs, 7, ids, off, sp, o, so)
     torch.cuda.synchronize()
     assert np.array_equal(h.float().cpu().numpy(), g["h"])
     assert np.array_equal(hs.float().cpu().numpy(), g["shared_h"])
