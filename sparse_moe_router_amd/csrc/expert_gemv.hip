@@ -267,11 +267,13 @@ static hipError_t dispatch_act(const FfnArgs& a, bool gateup, hipStream_t s) {
 
 hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (mfma_ok(a)) return launch_mfma_gateup(a, s);
   return a.qfmt == MOE_Q4_SYM_G32 ? dispatch_act<MOE_Q4_SYM_G32>(a, true, s) : dispatch_act<MOE_Q2_ASYM_G32>(a, true, s);
 }
 
 hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (mfma_ok(a)) return launch_mfma_down(a, s);
   return a.qfmt == MOE_Q4_SYM_G32 ? dispatch_act<MOE_Q4_SYM_G32>(a, false, s) : dispatch_act<MOE_Q2_ASYM_G32>(a, false, s);
 }
 

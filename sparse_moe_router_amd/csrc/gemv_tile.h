@@ -1,20 +1,19 @@
 // Dequantising dot products of packed group-32 rows with bf16 / fp32
 // activations, shared by the expert kernels (wave64, gfx950).
 //
-// Inner product of one group (bf16 activations): each code u becomes the exact
-// bf16 number 128 + u by OR-ing it into the mantissa of 0x4300 (=128), two
-// codes per 32-bit word, and v_dot2_f32_bf16 multiplies the pair with a pair
-// of activations in fp32 (products of an 8-bit code and a bf16 value are exact
-// in fp32).  The offset is removed with a per-group constant computed once per
-// token:  sum (u - 8) x = sum (128 + u) x - 136 sum x   (4-bit),
-//         sum u x       = sum (128 + u) x - 128 sum x   (2-bit),
-// and the group scale (and 2-bit minimum) is applied once per group:
-//         acc += s * sum(q x)            (4-bit, w = s q)
-//         acc += s * sum(u x) + m sum x  (2-bit, w = s u + m).
-// Activation pairs are pre-arranged per token to match the code pairs a mask
-// and a shift produce: 4-bit word i of a group yields pairs (8i+j, 8i+4+j) for
-// j = 0..3 from nibbles j and j+4; 2-bit word i yields pairs (16i+j, 16i+8+j)
-// for j = 0..7 from crumbs j and j+8.
+// Inner product of one group (bf16 activations): each code u is OR-ed into the
+// top mantissa bits of bf16 1.0, giving the exact bf16 number 1 + u/16 (4-bit)
+// or 1 + u/4 (2-bit), two codes per 32-bit word, and v_dot2_f32_bf16 multiplies
+// the pair with a pair of activations in fp32 (every product is exact).  The
+// offset is removed with a per-group constant computed once per token:
+//   4-bit:  D = sum (1 + u/16) x - 1.5 sum x = sum (u - 8) x / 16,  acc += 16 s D
+//   2-bit:  D = sum (1 + u/4) x - sum x      = sum u x / 4,         acc += 4 s D + m sum x
+// (w = s q with q = u - 8, or w = s u + m).  With the code in the top mantissa
+// bits the cancelled offset stays within a few times the signal, so the fp32
+// sums lose little to the cancellation.  Activation pairs are pre-arranged per
+// token to match the code pairs a mask and a shift produce: 4-bit word i of a
+// group yields pairs (8i+j, 8i+4+j) for j = 0..3 from nibbles j and j+4; 2-bit
+// word i yields pairs (16i+j, 16i+8+j) for j = 0..7 from crumbs j and j+8.
 #pragma once
 
 #include "moe_device.h"
@@ -35,7 +34,7 @@ template <int QF, int ACT> struct XGroup;
 template <int QF> struct XGroup<QF, MOE_ACT_BF16> {
   uint4 q[4];      // the group's 32 raw bf16 values
   uint32_t p[16];  // bf16 pairs matching the code pairs
-  float c;         // 136 * sum x (4-bit) or 128 * sum x (2-bit)
+  float c;         // 1.5 sum x (4-bit) or sum x (2-bit)
   float sx;        // sum x (2-bit only)
 
   __device__ __forceinline__ void load_raw(const void* base, size_t elem) {
@@ -64,19 +63,15 @@ template <int QF> struct XGroup<QF, MOE_ACT_BF16> {
         }
       }
     }
-    constexpr uint32_t kOff = (QF == MOE_Q4_SYM_G32) ? 0x43084308u : 0x43004300u;  // (136,136) / (128,128)
-    float c0 = 0.f, c1 = 0.f, s0 = 0.f, s1 = 0.f;
+    constexpr uint32_t kOff = (QF == MOE_Q4_SYM_G32) ? 0x3fc03fc0u : 0x3f803f80u;  // (1.5, 1.5) / (1, 1)
+    float c0 = 0.f, c1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       c0 = dot2_bf16(kOff, p[i], c0);
       c1 = dot2_bf16(kOff, p[i + 1], c1);
-      if constexpr (QF == MOE_Q2_ASYM_G32) {
-        s0 = dot2_bf16(0x3f803f80u, p[i], s0);
-        s1 = dot2_bf16(0x3f803f80u, p[i + 1], s1);
-      }
     }
     c = c0 + c1;
-    sx = s0 + s1;
+    sx = c;  // used by the 2-bit format only, where c = sum x
   }
 };
 
@@ -110,7 +105,11 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   return d;
 }
 
-// sum over the group of q*x (4-bit, q = u - 8) or u*x (2-bit).
+// Crumb j (bits 2j, 2j+1) moved to bits 5..6 (and crumb j + 8 to bits 21..22).
+__device__ __forceinline__ uint32_t shift_crumb(uint32_t w, int j) { return j <= 2 ? w << (5 - 2 * j) : w >> (2 * j - 5); }
+
+// bf16 activations: sum q x / 16 (4-bit, q = u - 8) or sum u x / 4 (2-bit);
+// fp32 activations: sum q x or sum u x.
 template <int QF, int ACT>
 __device__ __forceinline__ float group_dot(const typename CodeOf<QF>::T& cw, const XGroup<QF, ACT>& x) {
   if constexpr (ACT == MOE_ACT_BF16) {
@@ -122,11 +121,11 @@ __device__ __forceinline__ float group_dot(const typename CodeOf<QF>::T& cw, con
 #pragma unroll
       for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(w[i]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        d0 = dot2_bf16(and_or(w[i], 0x000f000fu, 0x43004300u), x.p[4 * i + 0], d0);
-        d1 = dot2_bf16(and_or(w[i] >> 4, 0x000f000fu, 0x43004300u), x.p[4 * i + 1], d1);
-        d0 = dot2_bf16(and_or(w[i] >> 8, 0x000f000fu, 0x43004300u), x.p[4 * i + 2], d0);
-        d1 = dot2_bf16(and_or(w[i] >> 12, 0x000f000fu, 0x43004300u), x.p[4 * i + 3], d1);
+      for (int i = 0; i < 4; ++i) {  // nibbles j, j + 4 -> bits 3..6, 19..22
+        d0 = dot2_bf16(and_or(w[i] << 3, 0x00780078u, 0x3f803f80u), x.p[4 * i + 0], d0);
+        d1 = dot2_bf16(and_or(w[i] >> 1, 0x00780078u, 0x3f803f80u), x.p[4 * i + 1], d1);
+        d0 = dot2_bf16(and_or(w[i] >> 5, 0x00780078u, 0x3f803f80u), x.p[4 * i + 2], d0);
+        d1 = dot2_bf16(and_or(w[i] >> 9, 0x00780078u, 0x3f803f80u), x.p[4 * i + 3], d1);
       }
     } else {
       uint32_t w[2] = {cw[0], cw[1]};
@@ -135,9 +134,9 @@ __device__ __forceinline__ float group_dot(const typename CodeOf<QF>::T& cw, con
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          d0 = dot2_bf16(and_or(w[i] >> (2 * j), 0x00030003u, 0x43004300u), x.p[8 * i + j], d0);
-          d1 = dot2_bf16(and_or(w[i] >> (2 * j + 2), 0x00030003u, 0x43004300u), x.p[8 * i + j + 1], d1);
+        for (int j = 0; j < 8; j += 2) {  // crumbs j, j + 8 -> bits 5..6, 21..22
+          d0 = dot2_bf16(and_or(shift_crumb(w[i], j), 0x00600060u, 0x3f803f80u), x.p[8 * i + j], d0);
+          d1 = dot2_bf16(and_or(shift_crumb(w[i], j + 1), 0x00600060u, 0x3f803f80u), x.p[8 * i + j + 1], d1);
         }
       }
     }
@@ -173,7 +172,9 @@ template <int QF, int ACT>
 __device__ __forceinline__ float group_acc(float acc, const typename CodeOf<QF>::T& cw, uint16_t s16, uint16_t m16,
                                            const XGroup<QF, ACT>& x) {
   const float d = group_dot<QF, ACT>(cw, x);
-  acc = fmaf(f16_to_f32(s16), d, acc);
+  // the bf16 path's sums carry a factor 1/16 or 1/4, folded into the scale (exactly)
+  constexpr float kUnit = ACT == MOE_ACT_BF16 ? (QF == MOE_Q4_SYM_G32 ? 16.f : 4.f) : 1.f;
+  acc = fmaf(f16_to_f32(s16) * kUnit, d, acc);
   if constexpr (QF == MOE_Q2_ASYM_G32) acc = fmaf(f16_to_f32(m16), x.sx, acc);
   return acc;
 }

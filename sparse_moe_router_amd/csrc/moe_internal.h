@@ -64,6 +64,11 @@ struct FfnArgs {
 };
 hipError_t launch_gateup(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
+// matrix-core grouped GEMMs for many tokens per expert (launch_gateup and
+// launch_down take this path themselves when mfma_ok holds)
+bool mfma_ok(const FfnArgs& a);
+hipError_t launch_mfma_gateup(const FfnArgs& a, hipStream_t s);
+hipError_t launch_mfma_down(const FfnArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- combine
 struct CombineArgs {

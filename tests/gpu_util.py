@@ -133,8 +133,8 @@ def certify_h(ld, xv, gpu, tokens_of_rows, experts_of_rows, h_gpu, h_ref, v_ref,
     Error model of the GPU's fp32 evaluation of v = silu(g) u:
     dv <= |silu'(g) u| e_g + |silu(g)| e_u + 2^-20 |v|, with the dot-product
     error e_g <= 2^-12 sum_i |W_g[r,i] x_i| (a generous multiple of the
-    2^-24-per-operation bound that also covers the 128-offset code encoding),
-    likewise e_u.  Near-cancelling g or u make v small and its relative error
+    2^-24-per-operation bound that also covers the offset code encoding,
+    whose cancelled offset is up to 1.5 sum |x|), likewise e_u.  Near-cancelling g or u make v small and its relative error
     large, so several storage steps can separate the two roundings there.
     Returns the number of differing elements."""
     act = ld.spec.act
@@ -178,5 +178,11 @@ def check_y_teacher_forced(ld, xv, gpu, tol=2e-3):
     r, rms = rel_err(gpu["y"], forced["y"])
     assert rms > 0
     assert r <= tol, f"teacher-forced max|dy| = {r:.3e} x RMS(y) exceeds {tol}"
+    # the expert outputs themselves, per routed pair and for the shared expert
+    ro, _ = rel_err(gpu["expert_out"], forced["expert_out"])
+    assert ro <= tol, f"teacher-forced expert_out max|do| = {ro:.3e} x RMS exceeds {tol}"
+    if shared_h is not None and gpu.get("shared_out") is not None:
+        rs, _ = rel_err(gpu["shared_out"], forced["shared_out"])
+        assert rs <= tol, f"teacher-forced shared_out max|do| = {rs:.3e} x RMS exceeds {tol}"
     direct, _ = rel_err(gpu["y"], ref["y"])
     return r, direct, flips
