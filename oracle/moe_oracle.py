@@ -283,16 +283,21 @@ def residual_step(x, y):
 # helpers for comparing against an fp32 implementation of the router
 
 def router_error_bound(x, w_r, b):
-    """beta[t,e] = gamma_{H+1} (sum_i |W_r[e,i] x[t,i]| + |b_e|), gamma_n = n u / (1 - n u), u = 2^-24.
+    """beta[t,e] = gamma_{3H+1} ((1 + 2^-6) sum_i |W_r[e,i] x[t,i]| + |b_e|),
+    gamma_n = n u / (1 - n u), u = 2^-24.
 
-    Standard worst-case bound on the error of an fp32 dot product of length H
-    plus one bias add, in any summation order, with exact (float64) inputs.
+    Worst-case bound on the error of an fp32 evaluation of the logit with exact
+    (float64-representable) inputs, in any summation order: either an fp32 dot
+    product of length H plus the bias, or the sum of 3 H exact products of x
+    with the three bf16 parts of each fp32 weight (hi + mid + lo = w exactly,
+    |hi| + |mid| + |lo| <= (1 + 2^-6) |w|) plus the bias.  The second form
+    has more terms, so its bound covers the first.
     """
     hdim = np.asarray(x).shape[-1]
-    n = hdim + 1
+    n = 3 * hdim + 1
     u = 2.0 ** -24
     gamma = n * u / (1 - n * u)
-    mag = np.abs(np.asarray(x, np.float64)) @ np.abs(np.asarray(w_r, np.float64)).T
+    mag = (1.0 + 2.0 ** -6) * (np.abs(np.asarray(x, np.float64)) @ np.abs(np.asarray(w_r, np.float64)).T)
     if b is not None:
         mag = mag + np.abs(np.asarray(b, np.float64))[None, :]
     return gamma * mag

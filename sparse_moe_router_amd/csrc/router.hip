@@ -74,6 +74,138 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// Many tokens (bf16 activations): the logits as a GEMM on the matrix cores.
+// Each fp32 router weight w is split exactly into three bf16 parts,
+//   hi = w truncated to bf16,  mid = (w - hi) truncated,  lo = w - hi - mid,
+// (every difference is exact in fp32 and lo has at most 8 significant bits),
+// so with bf16 x every product x * part is exact in fp32 and the MFMA chain
+// lo, mid, hi accumulates sum_k x_k w_k in fp32 like any fp32 dot product,
+// over 3 H exact terms.  The split is done in registers per 32-k step.
+// Block: 64 tokens x 64 experts, 4 waves; wave w owns experts n0 + 16 w ..
+// + 15 and all 64 tokens (4 MFMA tiles of 16 x 16); the x tile is staged
+// through LDS in 128-k chunks (double buffered), shared by the 4 waves.
+constexpr int kRouterMfmaMinTokens = 32;
+constexpr int kRM = 64, kRN = 64, kRKC = 128;
+constexpr int kRRow = kRKC + 8;  // bf16 per LDS row (+8: conflict-free 16-byte reads)
+
+typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float rf32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t ru32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ rf32x4_t router_mfma(ru32x4_t a, ru32x4_t b, rf32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rbf16x8_t, a), __builtin_bit_cast(rbf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// Two fp32 weights -> their hi, mid and lo bf16 parts, packed as pairs (element 0 low).
+__device__ __forceinline__ void split3(float w0, float w1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t b0 = __float_as_uint(w0), b1 = __float_as_uint(w1);
+  const float h0 = __uint_as_float(b0 & 0xffff0000u), h1 = __uint_as_float(b1 & 0xffff0000u);
+  const float r0 = w0 - h0, r1 = w1 - h1;
+  const uint32_t rb0 = __float_as_uint(r0), rb1 = __float_as_uint(r1);
+  const float m0 = __uint_as_float(rb0 & 0xffff0000u), m1 = __uint_as_float(rb1 & 0xffff0000u);
+  const uint32_t l0 = __float_as_uint(r0 - m0), l1 = __float_as_uint(r1 - m1);
+  hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // top halves: (b0 >> 16) | (b1 & 0xffff0000)
+  mid = __builtin_amdgcn_perm(rb1, rb0, 0x07060302u);
+  lo = __builtin_amdgcn_perm(l1, l0, 0x07060302u);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_router_mfma(RouterArgs a) {
+  __shared__ __align__(16) uint16_t s_x[2][kRM * kRRow];
+  const int m0 = blockIdx.x * kRM, n0 = blockIdx.y * kRN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ln = lane & 15, lc = lane >> 4;
+  const int nchunks = (a.H + kRKC - 1) / kRKC;
+
+  // staging: thread -> token row r = tid / 4, 32-k slice q = tid % 4 of the chunk (4 x 16 bytes)
+  const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
+  const uint16_t* xrow = reinterpret_cast<const uint16_t*>(a.x) + (size_t)min(m0 + r, a.T - 1) * a.H;
+  uint4 st[4];
+  auto load_x = [&](int kc) {
+    const int k = min(kc * kRKC + q * 32, a.H - 32);  // past H: any in-range slice, never used
+    const uint4* src = reinterpret_cast<const uint4*>(xrow + k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st[i] = src[i];
+  };
+  auto store_x = [&](int buf) {
+    uint4* dst = reinterpret_cast<uint4*>(&s_x[buf][r * kRRow + q * 32]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = st[i];
+  };
+
+  // B: this lane's expert row and k offset within a 32-k step
+  const int e = min(n0 + wave * 16 + ln, a.E - 1);
+  const float* wrow = a.w + (size_t)e * a.H + lc * 8;
+  rf32x4_t acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // this lane's 8 weights of each 32-k step of a chunk, prefetched one chunk ahead
+  float4 wv[4][2], wn[4][2];
+  auto load_w = [&](int kc, float4 (&w)[4][2]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = min(kc * kRKC + j * 32, a.H - 32);  // past H: any in-range step, never used
+      w[j][0] = *reinterpret_cast<const float4*>(wrow + k);
+      w[j][1] = *reinterpret_cast<const float4*>(wrow + k + 4);
+    }
+  };
+
+  load_x(0);
+  load_w(0, wv);
+  store_x(0);
+  __syncthreads();
+  for (int kc = 0; kc < nchunks; ++kc) {
+    const int buf = kc & 1;
+    const int steps = min(kRKC, a.H - kc * kRKC) / 32;  // H is a multiple of 32
+    if (kc + 1 < nchunks) {
+      load_x(kc + 1);
+      load_w(kc + 1, wn);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < steps) {
+        uint32_t h[4], m[4], l[4];
+        split3(wv[j][0].x, wv[j][0].y, h[0], m[0], l[0]);
+        split3(wv[j][0].z, wv[j][0].w, h[1], m[1], l[1]);
+        split3(wv[j][1].x, wv[j][1].y, h[2], m[2], l[2]);
+        split3(wv[j][1].z, wv[j][1].w, h[3], m[3], l[3]);
+        const ru32x4_t hi = {h[0], h[1], h[2], h[3]}, mid = {m[0], m[1], m[2], m[3]}, lo = {l[0], l[1], l[2], l[3]};
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const ru32x4_t xa = *reinterpret_cast<const ru32x4_t*>(&s_x[buf][(mt * 16 + ln) * kRRow + j * 32 + lc * 8]);
+          acc[mt] = router_mfma(xa, lo, acc[mt]);
+          acc[mt] = router_mfma(xa, mid, acc[mt]);
+          acc[mt] = router_mfma(xa, hi, acc[mt]);
+        }
+      }
+    }
+    if (kc + 1 < nchunks) {
+      store_x(buf ^ 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wv[j][0] = wn[j][0];
+        wv[j][1] = wn[j][1];
+      }
+    }
+    __syncthreads();
+  }
+
+  // D lane l holds tokens 4 (l / 16) + i of each M tile, expert ln of the wave's 16
+  const int en = n0 + wave * 16 + ln;
+  if (en < a.E) {
+    const float bias = a.b ? a.b[en] : 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = m0 + mt * 16 + lc * 4 + i;
+        if (t < a.T) a.logits[(size_t)t * a.E + en] = acc[mt][i] + bias;
+      }
+  }
+}
+
 // One wave per token, E <= 1024 (logits in registers).
 template <int PL>
 __global__ __launch_bounds__(256) void k_topk_regs(RouterArgs a) {
@@ -164,6 +296,10 @@ static void router_nch(const RouterArgs& a, dim3 grid, hipStream_t s) {
 
 hipError_t launch_router_logits(const RouterArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (a.act == MOE_ACT_BF16 && a.T >= kRouterMfmaMinTokens) {
+    k_router_mfma<<<dim3((a.T + kRM - 1) / kRM, (a.E + kRN - 1) / kRN), 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
   const int chunks = (a.T + 3) / 4;
   const dim3 grid((a.E + 3) / 4, a.T == 1 ? 1 : (chunks < 64 ? chunks : 64));
   if (a.T == 1) {

@@ -179,6 +179,36 @@ def test_many_tokens_per_expert(case):
     full_check(ld, x, strict=i >= 768)
 
 
+@pytest.mark.parametrize("shape", [(96, 70, 5, 100), (2048, 512, 10, 257), (4096, 64, 3, 40), (160, 1500, 7, 65)],
+                         ids=lambda c: "H{}_E{}_K{}_T{}".format(*c))
+def test_router_many_tokens(shape):
+    """Router logits on the matrix cores (>= 32 bf16 tokens): ragged token and
+    expert tiles, H not a multiple of the 128-wide staging chunk, E > 1024."""
+    h, e, k, t = shape
+    spec = synth.LayerSpec("router", h, e, k, 64, t, "q4_sym_g32", "bf16", h ** -0.5, 1.1, family=72 + h + e)
+    ld = synth.gen_layer(spec, routed_ids=[0])
+    x = synth.gen_x(spec)
+    L = gu.device_layer(synth.LayerData(spec, 0, ld.router_w, ld.router_b, _repeat_expert(ld.routed, e), ld.shared))
+    xd = gu.x_dev(x, spec.act)
+    ids = torch.empty((t, k), dtype=torch.int32, device=gu.DEV)
+    w = torch.empty((t, k), dtype=torch.float32, device=gu.DEV)
+    logits = torch.empty((t, e), dtype=torch.float32, device=gu.DEV)
+    api.moe_router_topk(L, xd, t, ids, w, logits)
+    torch.cuda.synchronize()
+    g = dict(logits=logits.cpu().numpy(), ids=ids.cpu().numpy().astype(np.int64), w=w.cpu().numpy())
+    differs = gu.check_routing(ld, x.values, g)
+    exact = mo.router_logits(x.values, ld.router_w, ld.router_b)
+    mag = np.abs(x.values.astype(np.float64)) @ np.abs(ld.router_w.astype(np.float64)).T
+    gu.say(f"  max |dlogit| / sum|Wx| = {(np.abs(g['logits'] - exact) / mag).max():.2e}; certified differing tokens {differs}")
+
+
+def _repeat_expert(es, n):
+    """n experts that all alias expert 0 of `es` (the router test needs only valid expert pointers)."""
+    rep = lambda m: synth.PackedMat(np.repeat(m.codes, n, 0), np.repeat(m.scales, n, 0),
+                                    None if m.mins is None else np.repeat(m.mins, n, 0))
+    return synth.ExpertSet(rep(es.gate), rep(es.up), rep(es.down), np.arange(n))
+
+
 def test_two_hot_experts_many_tiles():
     """Every token on experts 11 and 3: 300 rows each, five 64-row tiles per expert."""
     spec = synth.LayerSpec("hot2", 256, 16, 2, 256, 300, "q4_sym_g32", "bf16", 0.01, 1.1, family=69)
@@ -375,6 +405,37 @@ def test_verify_layer():
     gu.say("verify: T5 E512 K10 q2")
     g, r = full_check(ld, x)
     gu.say(f"verify max|dy|/rms = {r:.2e}; distinct experts {len(np.unique(g['ids']))}")
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_stack_forward_layer_by_layer(T):
+    """moe_stack_forward over 4 layers (residual x <- bf16(x + y)) equals the
+    layers run one by one, bitwise; each layer is checked against the oracle fed
+    the GPU's input to that layer (ids certified, y at the 2e-3 bar, x_next exact)."""
+    n = 4
+    spec = synth.LayerSpec("stack", 1024, 32, 4, 768, T, "q2_asym_g32", "bf16", 1024 ** -0.5, 1.1, family=71,
+                           n_layers=n)
+    lds = [synth.gen_layer(spec, layer=l) for l in range(n)]
+    Ls = [gu.device_layer(ld) for ld in lds]
+    x0 = gu.x_dev(synth.gen_x(spec), spec.act)
+    xs = x0.clone()
+    ws = api.workspace(Ls[0], T, gu.DEV)
+    y_last = torch.empty((T, spec.hidden), dtype=torch.float32, device=gu.DEV)
+    api.moe_stack_forward(Ls, xs, T, y_last, ws)
+    torch.cuda.synchronize()
+    cur = x0.clone()
+    for l, (ld, L) in enumerate(zip(lds, Ls)):
+        xin = cur.float().cpu().numpy().astype(np.float64)
+        g = gu.run_steps(L, cur, T)
+        gu.check_routing(ld, xin, g)
+        _, r = gu.check_y(ld, xin, g)
+        f = gu.run_forward(L, cur, T, x_next=True)
+        assert np.array_equal(f["y"], g["y"])
+        assert np.array_equal(f["x_next"].float().numpy().astype(np.float64), mo.residual_step(xin, f["y"]))
+        gu.say(f"  stack layer {l}: max|dy|/rms {r:.2e}")
+        cur = f["x_next"].to(gu.DEV)
+    assert torch.equal(xs.view(torch.int16), cur.view(torch.int16))
+    assert np.array_equal(y_last.cpu().numpy(), f["y"])
 
 
 @pytest.mark.parametrize("T", [7, 400])
