@@ -32,6 +32,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 64;          // tokens per tile
+constexpr int kXcdTiles = 4;     // tiles per XCD work group
 constexpr int kChunkG = 4;       // groups (of 32 k) per staged chunk
 constexpr int kRowWords = kChunkG * 16 + 4;  // LDS words per token row per chunk (+4 pad: no bank conflicts)
 
@@ -66,15 +67,25 @@ __device__ __forceinline__ void unpack_b(uint32_t w, uint32_t (&b)[4]) {
 // from the expert offsets (a wave-wide scan of the per-expert tile counts), so
 // the tiling needs no list in memory.  Returns false past the last tile.
 __device__ __forceinline__ bool find_tile(const FfnArgs& a, bool with_shared, int t, int& expert, int& m0) {
+  constexpr int kPer = 16;  // experts per lane per pass (one pass up to E = 1024)
   const int lane = threadIdx.x & 63;
   const int per = (a.E + 63) / 64;
-  const int e0 = lane * per;
+  const int e0 = lane * per, e_end = min(e0 + per, a.E);
+  // offsets of this lane's experts, all requested at once; indices past the
+  // lane's range repeat its last offset (no tiles)
+  auto counts = [&](int base, int (&c)[kPer]) {
+    int v[kPer + 1];
+#pragma unroll
+    for (int i = 0; i <= kPer; ++i) v[i] = a.offsets[min(e0 + base + i, e_end)];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) c[i] = (v[i + 1] - v[i] + kBM - 1) / kBM;
+  };
+  int c[kPer];
   int cnt = 0;
-  int prev = a.offsets[min(e0, a.E)];
-  for (int i = 0; i < per; ++i) {
-    const int nx = a.offsets[min(e0 + i + 1, a.E)];  // past E: nx == prev, no tiles
-    cnt += (nx - prev + kBM - 1) / kBM;
-    prev = nx;
+  for (int base = 0; base < per; base += kPer) {
+    counts(base, c);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) cnt += c[i];
   }
   int incl = cnt;
 #pragma unroll
@@ -90,16 +101,16 @@ __device__ __forceinline__ bool find_tile(const FfnArgs& a, bool with_shared, in
   }
   const int owner = __ffsll((unsigned long long)__ballot(incl > t)) - 1;
   int local = t - (incl - cnt), e_hit = 0, m_hit = 0;
-  prev = a.offsets[min(e0, a.E)];
-  for (int i = 0; i < per; ++i) {
-    const int nx = a.offsets[min(e0 + i + 1, a.E)];
-    const int c = (nx - prev + kBM - 1) / kBM;
-    if (local >= 0 && local < c) {
-      e_hit = e0 + i;
-      m_hit = local * kBM;
+  for (int base = 0; base < per; base += kPer) {
+    if (per > kPer) counts(base, c);  // one pass: the counts are still in registers
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (local >= 0 && local < c[i]) {
+        e_hit = e0 + base + i;
+        m_hit = local * kBM;
+      }
+      local -= c[i];
     }
-    local -= c;
-    prev = nx;
   }
   // uniform values: the matrix bases derived from them stay in scalar registers
   expert = __builtin_amdgcn_readfirstlane(__shfl(e_hit, owner));
@@ -114,8 +125,15 @@ __device__ __forceinline__ bool find_tile(const FfnArgs& a, bool with_shared, in
 // 64 tokens of the tile (4 x WN MFMA tiles per matrix).
 template <int QF, int NMAT, int WN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_expert_mfma(FfnArgs a, int with_shared, int n_blocks) {
-  // one-dimensional grid: block b works on tile b / n_blocks, output rows (b % n_blocks) * 64 WN + [0, 64 WN)
-  const int tile = blockIdx.x / n_blocks, nblk = blockIdx.x - tile * n_blocks;
+  // one-dimensional grid, a multiple of 8 groups of kXcdTiles tiles: block b
+  // runs on XCD b % 8; the work is dealt to the XCDs in groups of kXcdTiles
+  // consecutive tiles (all their row slices), so a group's blocks share one L2
+  // (the activation rows of a tile, the weights of an expert) and the groups
+  // spread evenly over the XCDs.
+  const int per_group = kXcdTiles * n_blocks;
+  const int slot = (int)(blockIdx.x >> 3), xcd = (int)(blockIdx.x & 7);
+  const int w = ((slot / per_group) * 8 + xcd) * per_group + slot % per_group;
+  const int tile = w / n_blocks, nblk = w - tile * n_blocks;
   int expert, m0;
   if (!find_tile(a, with_shared != 0, tile, expert, m0)) return;
   const bool shared = expert < 0;
@@ -167,22 +185,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     s_c[buf][jg][r] = QF == MOE_Q4_SYM_G32 ? -1.5f * sx : -sx;
   };
 
-  // ---- MFMA role
+  // ---- weights: the block's 256 row slots (NMAT x 64 WN rows) of codes and
+  // scales (and minima) of one chunk, copied global -> LDS by the DMA path
+  // (global_load_lds: lane i of an instruction lands at the wave-uniform LDS
+  // base + 16 i or + 4 i), double buffered.  Slot s: matrix s / (64 WN), row
+  // nblk * 64 WN + s % (64 WN) (clamped to the last row; never stored).
+  //   4-bit codes: per 16 slots 1 KiB laid out [group q][slot][16 B]
+  //   2-bit codes: per 32 slots 1 KiB laid out [group pair p][slot][16 B]
+  //   scales / minima: [slot][4 x fp16]
+  // With these layouts the MFMA lanes' reads below hit 64 distinct banks.
+  constexpr int kSlots = NMAT * 64 * WN;  // 256
+  constexpr int kCodeChunk = QF == MOE_Q4_SYM_G32 ? 64 : 32;  // code bytes per row per chunk
+  __shared__ __align__(16) uint8_t s_b[2][kSlots * kCodeChunk];
+  __shared__ __align__(16) uint16_t s_s[2][kSlots * kChunkG];
+  __shared__ __align__(16) uint16_t s_m[QF == MOE_Q2_ASYM_G32 ? 2 : 1][QF == MOE_Q2_ASYM_G32 ? kSlots * kChunkG : 8];
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 15, lc = lane >> 4;
-  const int nb = nblk * (64 * WN) + wave * (16 * WN);
   const int eidx = shared ? 0 : expert;
   constexpr int kCodeBytesPerGroup = QF == MOE_Q4_SYM_G32 ? 16 : 8;
-  constexpr int kLaneBytes = QF == MOE_Q4_SYM_G32 ? 4 : 2;  // one B lane: 8 codes
   const uint32_t row_bytes = (uint32_t)G * kCodeBytesPerGroup;
-  // the expert's matrices (uniform) and this lane's row offsets within them;
-  // gate and up share one layout, so one offset serves both
+  // the expert's matrices (uniform); pick field by field, since a reference
+  // into the argument block would force it into scratch
   const uint8_t* cb[NMAT];
   const uint16_t* sb[NMAT];
   const uint16_t* mb[NMAT];
 #pragma unroll
   for (int mi = 0; mi < NMAT; ++mi) {
-    // pick field by field: a reference into the argument block would force it into scratch
     const uint8_t* codes;
     const uint16_t *scales, *mins;
     if (NMAT == 1) {
@@ -202,38 +231,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     sb[mi] = scales + (size_t)eidx * rows * G;
     mb[mi] = QF == MOE_Q2_ASYM_G32 ? mins + (size_t)eidx * rows * G : nullptr;
   }
-  uint32_t coff[WN], soff[WN];
-  bool nok[WN];
+  auto slot_row = [&](int slot) { return (uint32_t)min(nblk * 64 * WN + slot % (64 * WN), rows - 1); };
+  // This wave's DMA sources: 4-bit codes, 4 instructions of 16 slots (lane ->
+  // slot 16 i + lane % 16, group lane / 16); 2-bit codes, 2 of 32 slots (lane
+  // -> slot 32 i + lane % 32, group pair lane / 32); scales (minima), 2 of 32
+  // slots (lane -> slot 32 i + lane / 2, group pair lane % 2).  Byte offsets
+  // within the chunk's first group; matrix per instruction (uniform).
+  constexpr int kCodeInst = QF == MOE_Q4_SYM_G32 ? 4 : 2;
+  uint32_t code_off[kCodeInst], scale_off[2];
 #pragma unroll
-  for (int nt = 0; nt < WN; ++nt) {
-    const int n = nb + nt * 16 + ln;
-    nok[nt] = n < rows;
-    const uint32_t rc = (uint32_t)min(n, rows - 1);
-    coff[nt] = rc * row_bytes + (uint32_t)lc * kLaneBytes;
-    soff[nt] = rc * (uint32_t)G;
+  for (int i = 0; i < kCodeInst; ++i) {
+    if constexpr (QF == MOE_Q4_SYM_G32) {
+      const int slot = (wave * 4 + i) * 16 + (lane & 15);
+      code_off[i] = slot_row(slot) * row_bytes + (uint32_t)(lane >> 4) * 16;
+    } else {
+      const int slot = (wave * 2 + i) * 32 + (lane & 31);
+      code_off[i] = slot_row(slot) * row_bytes + (uint32_t)(lane >> 5) * 16;
+    }
   }
-  // B operands of one chunk: a code word per (matrix, N tile, group); the 4
-  // fp16 scales (and minima) of the chunk's groups as one 8-byte load
-  struct BRegs {
-    uint32_t w[NMAT][WN][kChunkG];
-    uint2 s[NMAT][WN];
-    uint2 m[NMAT][WN];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int slot = (wave * 2 + i) * 32 + (lane >> 1);
+    scale_off[i] = (slot_row(slot) * (uint32_t)G + (uint32_t)(lane & 1) * 2) * 2;  // bytes
+  }
+  auto dma_b = [&](int kc, int buf) {
+#pragma unroll
+    for (int i = 0; i < kCodeInst; ++i) {
+      const int blk = wave * kCodeInst + i;  // 1 KiB block of the chunk buffer
+      const int mi = (blk * (QF == MOE_Q4_SYM_G32 ? 16 : 32)) / (64 * WN);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(cb[mi] + code_off[i] + (uint32_t)kc * kCodeChunk),
+                                       static_cast<void*>(&s_b[buf][blk * 1024]), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int blk = wave * 2 + i;  // 32 slots x 8 bytes
+      const int mi = (blk * 32) / (64 * WN);
+      const uint32_t off = scale_off[i] + (uint32_t)kc * (kChunkG * 2);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(reinterpret_cast<const uint8_t*>(sb[mi]) + off),
+                                       static_cast<void*>(&s_s[buf][blk * 128]), 4, 0, 0);
+      if constexpr (QF == MOE_Q2_ASYM_G32)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(reinterpret_cast<const uint8_t*>(mb[mi]) + off),
+                                         static_cast<void*>(&s_m[buf][blk * 128]), 4, 0, 0);
+    }
   };
-  auto load_b = [&](int kc, BRegs& b) {
-#pragma unroll
-    for (int mi = 0; mi < NMAT; ++mi)
-#pragma unroll
-      for (int nt = 0; nt < WN; ++nt) {
-#pragma unroll
-        for (int j = 0; j < kChunkG; ++j) {
-          const uint8_t* p = cb[mi] + coff[nt] + (uint32_t)(kc * kChunkG + j) * kCodeBytesPerGroup;
-          if constexpr (QF == MOE_Q4_SYM_G32) b.w[mi][nt][j] = *reinterpret_cast<const uint32_t*>(p);
-          else b.w[mi][nt][j] = *reinterpret_cast<const uint16_t*>(p);
-        }
-        b.s[mi][nt] = *reinterpret_cast<const uint2*>(sb[mi] + soff[nt] + kc * kChunkG);
-        if constexpr (QF == MOE_Q2_ASYM_G32) b.m[mi][nt] = *reinterpret_cast<const uint2*>(mb[mi] + soff[nt] + kc * kChunkG);
-      }
-  };
+
+  // MFMA lanes: this wave's output rows nb + nt * 16 + ln of each matrix
+  const int nb = nblk * (64 * WN) + wave * (16 * WN);
+  auto slot_of = [&](int mi, int nt) { return mi * 64 * WN + wave * 16 * WN + nt * 16 + ln; };
   auto half_of = [](uint2 v, int j) -> float {
     const uint32_t w = j < 2 ? v.x : v.y;
     return f16_to_f32((uint16_t)((j & 1) ? (w >> 16) : (w & 0xffffu)));
@@ -247,7 +291,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
       for (int nt = 0; nt < WN; ++nt) acc[mi][mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, const BRegs& b) {
+  auto compute = [&](int buf) {
+    uint2 sc4[NMAT][WN], mn4[NMAT][WN];
+#pragma unroll
+    for (int mi = 0; mi < NMAT; ++mi)
+#pragma unroll
+      for (int nt = 0; nt < WN; ++nt) {
+        sc4[mi][nt] = *reinterpret_cast<const uint2*>(&s_s[buf][slot_of(mi, nt) * kChunkG]);
+        if constexpr (QF == MOE_Q2_ASYM_G32) mn4[mi][nt] = *reinterpret_cast<const uint2*>(&s_m[buf][slot_of(mi, nt) * kChunkG]);
+      }
 #pragma unroll
     for (int j = 0; j < kChunkG; ++j) {
       uint32_t af[4][4];
@@ -258,16 +310,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         af[mt][0] = v.x; af[mt][1] = v.y; af[mt][2] = v.z; af[mt][3] = v.w;
         cf[mt] = *reinterpret_cast<const f32x4_t*>(&s_c[buf][j][mt * 16 + lc * 4]);
       }
+      uint32_t bw[NMAT][WN];
+#pragma unroll
+      for (int mi = 0; mi < NMAT; ++mi)
+#pragma unroll
+        for (int nt = 0; nt < WN; ++nt) {
+          const int slot = slot_of(mi, nt);
+          if constexpr (QF == MOE_Q4_SYM_G32) {
+            bw[mi][nt] = *reinterpret_cast<const uint32_t*>(&s_b[buf][(slot >> 4) * 1024 + j * 256 + (slot & 15) * 16 + lc * 4]);
+          } else {
+            bw[mi][nt] = *reinterpret_cast<const uint16_t*>(
+                &s_b[buf][(slot >> 5) * 1024 + (j >> 1) * 512 + (slot & 31) * 16 + (j & 1) * 8 + lc * 2]);
+          }
+        }
 #pragma unroll
       for (int mi = 0; mi < NMAT; ++mi)
 #pragma unroll
         for (int nt = 0; nt < WN; ++nt) {
           uint32_t bf[4];
-          unpack_b<QF>(b.w[mi][nt][j], bf);
-          // 16 s or 4 s (exact), and -m: sum x = -C on the D rows of this lane
-          const float sc = nok[nt] ? half_of(b.s[mi][nt], j) * (QF == MOE_Q4_SYM_G32 ? 16.f : 4.f) : 0.f;
+          unpack_b<QF>(bw[mi][nt], bf);
+          // s, and -m/4 (sum x = -C on the D rows of this lane); the factor 16
+          // or 4 of the codes is applied once in the epilogue (exactly)
+          const float sc = half_of(sc4[mi][nt], j);
           float mn = 0.f;
-          if constexpr (QF == MOE_Q2_ASYM_G32) mn = nok[nt] ? -half_of(b.m[mi][nt], j) : 0.f;
+          if constexpr (QF == MOE_Q2_ASYM_G32) mn = half_of(mn4[mi][nt], j) * -0.25f;
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
             const f32x4_t d = mfma16(af[mt], bf, cf[mt]);
@@ -288,28 +354,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   };
 
-  // two chunks per trip so that each register buffer has a fixed name
-  BRegs b0, b1;
+  // the DMA writes LDS behind the compiler's back: wait for it (vmcnt) with a
+  // memory clobber before the barrier that publishes the chunk
+  auto wait_dma = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  dma_b(0, 0);
   load_a(0);
-  load_b(0, b0);
   store_a(0);
+  wait_dma();
   __syncthreads();
-  for (int kc = 0; kc < nchunks; kc += 2) {
-    const bool more1 = kc + 1 < nchunks, more2 = kc + 2 < nchunks;
-    if (more1) {
+  for (int kc = 0; kc < nchunks; ++kc) {
+    const int buf = kc & 1;
+    const bool more = kc + 1 < nchunks;
+    if (more) {
+      dma_b(kc + 1, buf ^ 1);
       load_a(kc + 1);
-      load_b(kc + 1, b1);
     }
-    compute(0, b0);
-    if (more1) store_a(1);
-    __syncthreads();
-    if (!more1) break;
-    if (more2) {
-      load_a(kc + 2);
-      load_b(kc + 2, b0);
-    }
-    compute(1, b1);
-    if (more2) store_a(0);
+    compute(buf);
+    if (more) store_a(buf ^ 1);
+    wait_dma();
     __syncthreads();
   }
 
@@ -324,11 +386,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const int m = m0 + mt * 16 + lc * 4 + i;
         if (m < n_rows && n < rows) {
           const size_t orow = shared ? (size_t)m : (size_t)(lo + m);
+          constexpr float kUnit = QF == MOE_Q4_SYM_G32 ? 16.f : 4.f;  // the codes' 1/16 or 1/4, exactly
           if constexpr (NMAT == 2) {
-            const float g = acc[0][mt][nt][i], u = acc[1][mt][nt][i];
+            const float g = acc[0][mt][nt][i] * kUnit, u = acc[1][mt][nt][i] * kUnit;
             store_act<MOE_ACT_BF16>(shared ? a.hs : a.h, orow * rows + n, silu(g) * u);
           } else {
-            (shared ? a.so : a.o)[orow * rows + n] = acc[0][mt][nt][i];
+            (shared ? a.so : a.o)[orow * rows + n] = acc[0][mt][nt][i] * kUnit;
           }
         }
       }
@@ -343,8 +406,7 @@ static int tile_capacity(const FfnArgs& a, bool with_shared) {
 
 // Matrix-core path: bf16 activations (the A operand is the activation
 // itself), on average at least 8 tokens per expert, H and I multiples of 128
-// (whole chunks of 4 groups) and 8-byte aligned scale and minimum arrays (one
-// load per row and chunk).
+// (whole chunks of 4 groups) and 8-byte aligned scale and minimum arrays.
 static bool al8(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 7) == 0; }
 static bool qm_al8(const QMat& q) { return al8(q.scales) && al8(q.mins); }
 
@@ -358,7 +420,8 @@ bool mfma_ok(const FfnArgs& a) {
 hipError_t launch_mfma_gateup(const FfnArgs& a, hipStream_t s) {
   const bool ws = a.n_shared && a.hs;
   const int nb = (a.I + 127) / 128;  // 4 waves x 2 N tiles of 16 rows of I
-  const dim3 grid((unsigned)((int64_t)nb * tile_capacity(a, ws)));
+  const int64_t unit = (int64_t)8 * kXcdTiles * nb;
+  const dim3 grid((unsigned)(((int64_t)nb * tile_capacity(a, ws) + unit - 1) / unit * unit));
   if (a.qfmt == MOE_Q4_SYM_G32) k_expert_mfma<MOE_Q4_SYM_G32, 2, 2><<<grid, 256, 0, s>>>(a, ws, nb);
   else k_expert_mfma<MOE_Q2_ASYM_G32, 2, 2><<<grid, 256, 0, s>>>(a, ws, nb);
   return hipGetLastError();
@@ -367,7 +430,8 @@ hipError_t launch_mfma_gateup(const FfnArgs& a, hipStream_t s) {
 hipError_t launch_mfma_down(const FfnArgs& a, hipStream_t s) {
   const bool ws = a.n_shared && a.so;
   const int nb = (a.H + 255) / 256;  // 4 waves x 4 N tiles of 16 rows of H
-  const dim3 grid((unsigned)((int64_t)nb * tile_capacity(a, ws)));
+  const int64_t unit = (int64_t)8 * kXcdTiles * nb;
+  const dim3 grid((unsigned)(((int64_t)nb * tile_capacity(a, ws) + unit - 1) / unit * unit));
   if (a.qfmt == MOE_Q4_SYM_G32) k_expert_mfma<MOE_Q4_SYM_G32, 1, 4><<<grid, 256, 0, s>>>(a, ws, nb);
   else k_expert_mfma<MOE_Q2_ASYM_G32, 1, 4><<<grid, 256, 0, s>>>(a, ws, nb);
   return hipGetLastError();
