@@ -300,53 +300,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         sc4[mi][nt] = *reinterpret_cast<const uint2*>(&s_s[buf][slot_of(mi, nt) * kChunkG]);
         if constexpr (QF == MOE_Q2_ASYM_G32) mn4[mi][nt] = *reinterpret_cast<const uint2*>(&s_m[buf][slot_of(mi, nt) * kChunkG]);
       }
-#pragma unroll
-    for (int j = 0; j < kChunkG; ++j) {
+    struct GroupOps {
       uint32_t af[4][4];
       f32x4_t cf[4];
+      uint32_t bw[NMAT][WN];
+    };
+    auto lds_group = [&](int j, GroupOps& g) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const uint4 v = *reinterpret_cast<const uint4*>(&s_a[buf][(mt * 16 + ln) * kRowWords + j * 16 + lc * 4]);
-        af[mt][0] = v.x; af[mt][1] = v.y; af[mt][2] = v.z; af[mt][3] = v.w;
-        cf[mt] = *reinterpret_cast<const f32x4_t*>(&s_c[buf][j][mt * 16 + lc * 4]);
+        g.af[mt][0] = v.x; g.af[mt][1] = v.y; g.af[mt][2] = v.z; g.af[mt][3] = v.w;
+        g.cf[mt] = *reinterpret_cast<const f32x4_t*>(&s_c[buf][j][mt * 16 + lc * 4]);
       }
-      uint32_t bw[NMAT][WN];
 #pragma unroll
       for (int mi = 0; mi < NMAT; ++mi)
 #pragma unroll
         for (int nt = 0; nt < WN; ++nt) {
           const int slot = slot_of(mi, nt);
           if constexpr (QF == MOE_Q4_SYM_G32) {
-            bw[mi][nt] = *reinterpret_cast<const uint32_t*>(&s_b[buf][(slot >> 4) * 1024 + j * 256 + (slot & 15) * 16 + lc * 4]);
+            g.bw[mi][nt] = *reinterpret_cast<const uint32_t*>(&s_b[buf][(slot >> 4) * 1024 + j * 256 + (slot & 15) * 16 + lc * 4]);
           } else {
-            bw[mi][nt] = *reinterpret_cast<const uint16_t*>(
+            g.bw[mi][nt] = *reinterpret_cast<const uint16_t*>(
                 &s_b[buf][(slot >> 5) * 1024 + (j >> 1) * 512 + (slot & 31) * 16 + (j & 1) * 8 + lc * 2]);
           }
         }
+    };
+    GroupOps gops[2];
+    lds_group(0, gops[0]);
+#pragma unroll
+    for (int j = 0; j < kChunkG; ++j) {
+      if (j + 1 < kChunkG) lds_group(j + 1, gops[(j + 1) & 1]);  // next group's operands in flight
+      auto& af = gops[j & 1].af;
+      auto& cf = gops[j & 1].cf;
+      auto& bw = gops[j & 1].bw;
+      // software pipeline over the NW (matrix, N tile) pairs: the products of
+      // pair p are issued before the scaling of pair p - 1
+      constexpr int NW = NMAT * WN;
+      f32x4_t dp[4];
+      float scp = 0.f, mnp = 0.f;
+#pragma unroll
+      for (int p = 0; p <= NW; ++p) {
+        f32x4_t dc[4];
+        float scc = 0.f, mnc = 0.f;
+        if (p < NW) {
+          const int mi = p / WN, nt = p % WN;
+          uint32_t bf[4];
+          unpack_b<QF>(bw[mi][nt], bf);
+          scc = half_of(sc4[mi][nt], j);
+          if constexpr (QF == MOE_Q2_ASYM_G32) mnc = half_of(mn4[mi][nt], j) * -0.25f;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) dc[mt] = mfma16(af[mt], bf, cf[mt]);
+        }
+        if (p > 0) {
+          const int mi = (p - 1) / WN, nt = (p - 1) % WN;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mi][mt][nt][i] = fmaf(scp, dp[mt][i], acc[mi][mt][nt][i]);
+            if constexpr (QF == MOE_Q2_ASYM_G32) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[mi][mt][nt][i] = fmaf(mnp, cf[mt][i], acc[mi][mt][nt][i]);
+            }
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) dp[mt] = dc[mt];
+        scp = scc;
+        mnp = mnc;
+      }
 #pragma unroll
       for (int mi = 0; mi < NMAT; ++mi)
 #pragma unroll
-        for (int nt = 0; nt < WN; ++nt) {
-          uint32_t bf[4];
-          unpack_b<QF>(bw[mi][nt], bf);
-          // s, and -m/4 (sum x = -C on the D rows of this lane); the factor 16
-          // or 4 of the codes is applied once in the epilogue (exactly)
-          const float sc = half_of(sc4[mi][nt], j);
-          float mn = 0.f;
-          if constexpr (QF == MOE_Q2_ASYM_G32) mn = half_of(mn4[mi][nt], j) * -0.25f;
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const f32x4_t d = mfma16(af[mt], bf, cf[mt]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mi][mt][nt][i] = fmaf(sc, d[i], acc[mi][mt][nt][i]);
-            if constexpr (QF == MOE_Q2_ASYM_G32) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[mi][mt][nt][i] = fmaf(mn, cf[mt][i], acc[mi][mt][nt][i]);
-            }
-          }
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) asm volatile("" : "+v"(acc[mi][mt][nt]));
-        }
+          for (int nt = 0; nt < WN; ++nt) asm volatile("" : "+v"(acc[mi][mt][nt]));
       // (the empty asm statements above keep each product's scaling next to
       // it: left alone, the compiler sinks the scaling past later groups'
       // products and holds every product's result at once)
@@ -376,23 +403,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
 
   // ---- epilogue: D lane l holds token rows 4 (l / 16) + i of each M tile, column ln
+  constexpr float kUnit = QF == MOE_Q4_SYM_G32 ? 16.f : 4.f;  // the codes' 1/16 or 1/4, exactly
+  const bool all_rows = (nblk + 1) * (64 * WN) <= rows;  // uniform: no row of this block is past the end
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < WN; ++nt) {
-      const int n = nb + nt * 16 + ln;
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + mt * 16 + lc * 4 + i;
+      if (m >= n_rows) continue;
+      const size_t orow = shared ? (size_t)m : (size_t)(lo + m);
+      if constexpr (NMAT == 2) {
+        uint16_t* hrow = reinterpret_cast<uint16_t*>(shared ? a.hs : a.h) + orow * rows;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + mt * 16 + lc * 4 + i;
-        if (m < n_rows && n < rows) {
-          const size_t orow = shared ? (size_t)m : (size_t)(lo + m);
-          constexpr float kUnit = QF == MOE_Q4_SYM_G32 ? 16.f : 4.f;  // the codes' 1/16 or 1/4, exactly
-          if constexpr (NMAT == 2) {
+        for (int nt = 0; nt < WN; ++nt) {
+          const int n = nb + nt * 16 + ln;
+          if (all_rows || n < rows) {
             const float g = acc[0][mt][nt][i] * kUnit, u = acc[1][mt][nt][i] * kUnit;
-            store_act<MOE_ACT_BF16>(shared ? a.hs : a.h, orow * rows + n, silu(g) * u);
-          } else {
-            (shared ? a.so : a.o)[orow * rows + n] = acc[0][mt][nt][i] * kUnit;
+            // silu(g) = g / (1 + e^-g), the quotient as a product with the
+            // hardware reciprocal (within 2 ulp: far below the bf16 rounding)
+            const float sg = g * __builtin_amdgcn_rcpf(1.0f + expf(-g));
+            hrow[n] = f32_to_bf16(sg * u);
           }
+        }
+      } else {
+        float* orow_p = (shared ? a.so : a.o) + orow * rows;
+#pragma unroll
+        for (int nt = 0; nt < WN; ++nt) {
+          const int n = nb + nt * 16 + ln;
+          if (all_rows || n < rows) orow_p[n] = acc[0][mt][nt][i] * kUnit;
         }
       }
     }

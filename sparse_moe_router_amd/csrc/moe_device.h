@@ -10,13 +10,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// float -> bfloat16 bits, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// float -> bfloat16 bits, round to nearest even (v_cvt_pk_bf16_f32; NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
