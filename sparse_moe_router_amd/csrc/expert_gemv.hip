@@ -348,74 +348,57 @@ k_fused_gateup(RouterArgs r, PermuteArgs pm, FfnArgs a, int lpr_log2) {
 }
 
 // One token: down projection of the shared expert and the K selected experts
-// for the wave's rows, combined in slot order in registers:
+// for the block's RPI rows, combined in slot order:
 //   y[r] = o_shared[r] + sum_k w[k] o_k[r]   (the arithmetic of k_down + k_combine)
-// The K + 1 rows of h are staged in LDS once per block; the routing values are
-// read with scalar loads so they do not queue behind the vector loads.
-template <int QF, int KMAX, int RPW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_fused_down1(FfnArgs a,
-                                                                                             CombineArgs c,
-                                                                                             int lpr_log2) {
-  extern __shared__ uint4 s_h[];  // rows 0..K-1: h in sorted order; row K: the shared expert's h
-  const int K = a.K, I = a.I, row16 = I / 8;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// The slots are split over the block's 4 waves (wave w takes slots w, w + 4,
+// ...; the shared expert is slot K), so that four waves per row group keep
+// the memory and the reductions busy; each wave reads its slots' weight rows
+// and h groups directly, the products meet in LDS and wave 0 combines them.
+// The routing values are read with scalar loads.
+template <int QF, int SPW>
+__global__ __launch_bounds__(256) void k_fused_down1(FfnArgs a, CombineArgs c, int lpr_log2) {
+  __shared__ float s_o[4 * SPW][64];  // [slot][row of the block]
+  const int K = a.K, I = a.I;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
   const int sub = lane & (LPR - 1), rsub = lane >> lpr_log2;
   const int G = I / kGroup;
-  const int rbase = (blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave)) * RPW * RPI;
+  const int rbase = blockIdx.x * RPI;
   const bool has_shared = a.so != nullptr;  // the shared expert is present
-  // 1. routing of the token (uniform scalar loads) and every slot's weight rows
-  int pos[KMAX];
-  float wgt[KMAX];
-  RowTile<QF, RPW, 1> tw[KMAX + 1];
+  const int nslots = K + (has_shared ? 1 : 0);
+  const int gc = min(sub, G - 1);
+  // 1. this wave's slots: weight rows and the matching h groups, all requested first
+  RowTile<QF, 1, 1> tw[SPW];
+  XGroup<QF, MOE_ACT_BF16> hg[SPW];
 #pragma unroll
-  for (int k = 0; k < KMAX; ++k) {
-    const int kk = min(k, K - 1);  // clamped: duplicates past K are loaded but unused
-    const int e = __builtin_amdgcn_readfirstlane(a.ids[kk]);
-    pos[k] = __builtin_amdgcn_readfirstlane(c.pair_pos[kk]);
-    wgt[k] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.w[kk])));
-    tw[k].load(expert_view<QF>(a.down, e, a.H, I), rbase, rsub, RPI, a.H, sub, LPR);
+  for (int j = 0; j < SPW; ++j) {
+    const int slot = min(wave + 4 * j, nslots - 1);  // clamped: slots past the end are loaded but unused
+    const bool sh = has_shared && slot == K;
+    const int e = sh ? 0 : __builtin_amdgcn_readfirstlane(a.ids[slot]);
+    const int hrow = sh ? 0 : __builtin_amdgcn_readfirstlane(c.pair_pos[slot]);
+    hg[j].load_raw(sh ? a.hs : a.h, (size_t)hrow * I + (size_t)gc * kGroup);
+    tw[j].load(expert_view<QF>(sh ? a.sdown : a.down, e, a.H, I), rbase, rsub, RPI, a.H, sub, LPR);
   }
-  if (has_shared) tw[KMAX].load(expert_view<QF>(a.sdown, 0, a.H, I), rbase, rsub, RPI, a.H, sub, LPR);
-  // 2. the h rows into LDS, in rounds of kStage 16-byte chunks per thread
-  constexpr int kStage = 5;
-  const int n16 = (K + (has_shared ? 1 : 0)) * row16;
-  for (int base = 0; base < n16; base += 256 * kStage) {
-    uint4 st[kStage];
+  // 2. o for each slot and row, into LDS
+  const bool gok = sub < G;
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      const int idx = min(base + (int)threadIdx.x + i * 256, n16 - 1);
-      const int slot = idx / row16, off = idx % row16;
-      const uint16_t* src = slot < K ? reinterpret_cast<const uint16_t*>(a.h) + (size_t)slot * I
-                                     : reinterpret_cast<const uint16_t*>(a.hs);
-      st[i] = reinterpret_cast<const uint4*>(src)[off];
-    }
-#pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      const int idx = base + (int)threadIdx.x + i * 256;
-      if (idx < n16) s_h[idx] = st[i];
-    }
+  for (int j = 0; j < SPW; ++j) {
+    const int slot = wave + 4 * j;
+    hg[j].prep();
+    const float v = group_acc<QF, MOE_ACT_BF16>(0.f, tw[j].c[0][0], tw[j].s[0][0], tw[j].m[0][0], hg[j]);
+    const float o = seg_sum(gok ? v : 0.f, LPR);
+    if (slot < nslots && sub == 0) s_o[slot][rsub] = o;
   }
   __syncthreads();
-  const bool gok = sub < G;
-  const int gc = min(sub, G - 1);
-  auto slot_out = [&](const RowTile<QF, RPW, 1>& t, int hrow, int rr) {
-    XGroup<QF, MOE_ACT_BF16> hg;
-    const uint4* src = s_h + (size_t)hrow * row16 + gc * 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hg.q[i] = src[i];
-    hg.prep();
-    const float v = group_acc<QF, MOE_ACT_BF16>(0.f, t.c[rr][0], t.s[rr][0], t.m[rr][0], hg);
-    return seg_sum(gok ? v : 0.f, LPR);
-  };
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    const int r = rbase + rsub + rr * RPI;
-    float acc = has_shared ? slot_out(tw[KMAX], K, rr) : 0.f;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-      if (k < K) acc = fmaf(wgt[k], slot_out(tw[k], pos[k], rr), acc);
-    if (sub == 0 && r < a.H) {
+  // 3. the combine, in slot order (shared first), by lane r of wave 0 for row rbase + r
+  if (wave == 0 && lane < RPI) {
+    const int r = rbase + lane;
+    float acc = has_shared ? s_o[K][lane] : 0.f;
+    for (int k = 0; k < K; ++k) {
+      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.w[k])));
+      acc = fmaf(w, s_o[k][lane], acc);
+    }
+    if (r < a.H) {
       c.y[r] = acc;
       if (c.x_next) store_act<MOE_ACT_BF16>(c.x_next, r, load_act<MOE_ACT_BF16>(c.x_resid, r) + acc);
     }
@@ -427,7 +410,7 @@ bool fused_decode_ok(int T, int K, int E, int H, int I, int act) {
          I <= 64 * kGroup;
 }
 
-bool fused_down1_ok(int T, int K, int I) { return T == 1 && K <= 16 && I <= 2048 && (K + 1) * I * 2 <= 65536; }
+bool fused_down1_ok(int T, int K, int I) { return T == 1 && K <= 16 && I <= 64 * kGroup; }
 
 template <int QF>
 static hipError_t fused_gateup_pl(const RouterArgs& r, const PermuteArgs& pm, const FfnArgs& a, hipStream_t s) {
@@ -469,14 +452,12 @@ static hipError_t fused_down1_q(const FfnArgs& a, const CombineArgs& c, hipStrea
   int lpr_log2, gpl;
   lane_split(a.I, &lpr_log2, &gpl);
   const int rpi = 64 >> lpr_log2;
-  constexpr int kRpwDown = 1;
-  const int rows_per_block = 4 * kRpwDown * rpi;
-  const dim3 grid((a.H + rows_per_block - 1) / rows_per_block);
-  const size_t lds = (size_t)(a.K + 1) * a.I * 2;
-  if (a.K <= 4) k_fused_down1<QF, 4, kRpwDown><<<grid, 256, lds, s>>>(a, c, lpr_log2);
-  else if (a.K <= 8) k_fused_down1<QF, 8, kRpwDown><<<grid, 256, lds, s>>>(a, c, lpr_log2);
-  else if (a.K <= 12) k_fused_down1<QF, 12, kRpwDown><<<grid, 256, lds, s>>>(a, c, lpr_log2);
-  else k_fused_down1<QF, 16, kRpwDown><<<grid, 256, lds, s>>>(a, c, lpr_log2);
+  const dim3 grid((a.H + rpi - 1) / rpi);
+  const int nslots = a.K + (a.so ? 1 : 0);
+  if (nslots <= 4) k_fused_down1<QF, 1><<<grid, 256, 0, s>>>(a, c, lpr_log2);
+  else if (nslots <= 8) k_fused_down1<QF, 2><<<grid, 256, 0, s>>>(a, c, lpr_log2);
+  else if (nslots <= 12) k_fused_down1<QF, 3><<<grid, 256, 0, s>>>(a, c, lpr_log2);
+  else k_fused_down1<QF, 5><<<grid, 256, 0, s>>>(a, c, lpr_log2);
   return hipGetLastError();
 }
 
