@@ -284,6 +284,7 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
 // (one token) down projection with the weighted combine.
 
 constexpr int kFusedMaxPairs = 128;
+constexpr int kFusedRpw1 = 2;  // rows per wave of the one-token fused gate/up
 
 // gate/up with the top-K and the stable token -> expert ordering recomputed in
 // every block from the router logits (2 KiB per token at E = 512): block row y
@@ -417,17 +418,18 @@ static hipError_t fused_gateup_pl(const RouterArgs& r, const PermuteArgs& pm, co
   int lpr_log2, gpl;
   lane_split(a.H, &lpr_log2, &gpl);
   const int rpi = 64 >> lpr_log2;
-  const int rows_per_block = 4 * kRPW * rpi;
+  // one token: 2 rows per wave (twice the blocks, each with less to stream after its routing)
+  const int rows_per_block = 4 * (a.T == 1 ? kFusedRpw1 : kRPW) * rpi;
   const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, a.T * a.K + (a.n_shared && a.hs ? 1 : 0));
   const int pl = regs_per_lane(a.E);
   auto go = [&](auto kern) { kern<<<grid, 256, 0, s>>>(r, pm, a, lpr_log2); };
   if (a.T == 1) {
     switch (pl) {
-      case 1: go(k_fused_gateup<QF, 1, 1, kRPW>); break;
-      case 2: go(k_fused_gateup<QF, 1, 2, kRPW>); break;
-      case 4: go(k_fused_gateup<QF, 1, 4, kRPW>); break;
-      case 8: go(k_fused_gateup<QF, 1, 8, kRPW>); break;
-      default: go(k_fused_gateup<QF, 1, 16, kRPW>); break;
+      case 1: go(k_fused_gateup<QF, 1, 1, kFusedRpw1>); break;
+      case 2: go(k_fused_gateup<QF, 1, 2, kFusedRpw1>); break;
+      case 4: go(k_fused_gateup<QF, 1, 4, kFusedRpw1>); break;
+      case 8: go(k_fused_gateup<QF, 1, 8, kFusedRpw1>); break;
+      default: go(k_fused_gateup<QF, 1, 16, kFusedRpw1>); break;
     }
   } else {
     switch (pl) {

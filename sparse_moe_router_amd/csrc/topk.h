@@ -27,10 +27,11 @@ __device__ __forceinline__ uint64_t sel_key(float l, int e) {
 __device__ __forceinline__ int key_id(uint64_t k) { return (int)(0xffffffffu - (uint32_t)k); }
 
 // Top-K of one token by one wave with the token's logits in registers
-// (expert e = lane + 64 i, PL per lane).  Each lane keeps its best remaining
-// candidate (largest key, lowest id on equal keys); a round takes the wave
-// maximum of the 32-bit keys (one DPP max per step), the owner of the winner
-// (the lowest id among lanes tied at the maximum) drops it and rescans.
+// (expert e = lane + 64 i, PL per lane).  Each lane first sorts its PL
+// candidates (64-bit keys: logit order, then lower id) in registers; a round
+// takes the wave maximum of the lanes' heads (32-bit logit keys, one DPP max
+// per step), the lowest id among lanes tied at the maximum wins, and the
+// winning lane shifts its sorted list by one.
 // Writes ids and the renormalised softmax weights of the K selected logits
 // (unless ids is null; then only lds_ids, which requires K <= 64).
 template <int PL>
@@ -39,42 +40,44 @@ __device__ __forceinline__ void wave_topk_regs(const float* lg, int E, int K, in
   float v[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) v[i] = lg[min(lane + 64 * i, E - 1)];  // clamped: no conditional loads
-  uint32_t key[PL];
+  uint64_t c[PL];  // (key << 32) | ~id; 0 = empty
 #pragma unroll
-  for (int i = 0; i < PL; ++i) key[i] = (lane + 64 * i < E) ? order_key(v[i]) : 0u;
-  // the lane's best: scanning i upward with a strict '>' keeps the lowest id on ties
-  auto rescan = [&](uint32_t* bk, int* bid) {
-    *bk = 0u; *bid = 0x7fffffff;
+  for (int i = 0; i < PL; ++i)
+    c[i] = (lane + 64 * i < E) ? sel_key(v[i], lane + 64 * i) : 0ull;
+  // odd-even transposition sort, descending (PL is small; every step is independent compare-swaps)
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const bool better = key[i] > *bk;
-      *bid = better ? lane + 64 * i : *bid;
-      *bk = better ? key[i] : *bk;
+  for (int pass = 0; pass < PL; ++pass) {
+#pragma unroll
+    for (int i = pass & 1; i + 1 < PL; i += 2) {
+      const uint64_t hi = c[i] > c[i + 1] ? c[i] : c[i + 1];
+      const uint64_t lo = c[i] > c[i + 1] ? c[i + 1] : c[i];
+      c[i] = hi;
+      c[i + 1] = lo;
     }
-  };
-  uint32_t bk;
-  int bid;
-  rescan(&bk, &bid);
+  }
   uint32_t mine = 0;   // lane k keeps the key and id picked in round k (k < 64)
   int mine_id = 0;
   uint32_t top = 0;
   for (int k = 0; k < K; ++k) {
+    const uint32_t bk = (uint32_t)(c[0] >> 32);
     const uint32_t m = wave_max_u32(bk);
     const uint64_t tied = __ballot(bk == m);
-    int id;
+    int winner;  // lane
     if (__popcll(tied) == 1) {
-      id = __builtin_amdgcn_readlane(bid, (int)__ffsll((unsigned long long)tied) - 1);
+      winner = (int)__ffsll((unsigned long long)tied) - 1;
     } else {  // several lanes hold an equal key: the lowest id wins
-      id = wave_min_i32(bk == m ? bid : 0x7fffffff);
+      const int id_min = wave_min_i32(bk == m ? key_id(c[0]) : 0x7fffffff);
+      winner = id_min & 63;
     }
+    const int id = (int)(0xffffffffu - (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)c[0], winner));
     if (k == 0) top = m;
     if (lane == (k & 63)) { mine = m; mine_id = id; }
     if (K > 64 && ids && lane == 0) ids[k] = id;
     if (lds_ids && lane == 0) lds_ids[k] = id;
-    if ((id & 63) == lane) {
+    if (lane == winner) {
 #pragma unroll
-      for (int i = 0; i < PL; ++i) key[i] = (lane + 64 * i == id) ? 0u : key[i];
-      rescan(&bk, &bid);
+      for (int i = 0; i + 1 < PL; ++i) c[i] = c[i + 1];
+      c[PL - 1] = 0ull;
     }
   }
   const float l0 = key_value(top);
