@@ -348,9 +348,46 @@ k_fused_gateup(RouterArgs r, PermuteArgs pm, FfnArgs a, int lpr_log2) {
   gateup_rows<QF, MOE_ACT_BF16, NT, 1, RPW>(a, wk, shared, rbase, lane >> lpr_log2, lane & (LPR - 1), lpr_log2, tok);
 }
 
+// One token: block row k < K computes the expert picked in selection round k
+// and writes h row k (h in slot order, as k_fused_down1 reads it); row K is
+// the shared expert.  Each wave runs the selection itself and stops after
+// round k, so the rows of the first picks stream their weights while the
+// later picks are still being selected.  The block at (0, K - 1) runs every
+// round and writes ids and weights as moe_router_topk does.
+template <int QF, int PL, int RPW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MOE_ACT_BF16, 1, 1)))) void
+k_fused_gateup1(RouterArgs r, FfnArgs a, int lpr_log2) {
+  const int K = a.K;
+  const int y = blockIdx.y;
+  const bool shared = y == K;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Work wk;
+  wk.lo = shared ? 0 : y; wk.n = 1; wk.pair0 = y; wk.expert = -1;
+  if (!shared) {
+    uint64_t c[PL];
+    lane_candidates<PL>(r.logits, r.E, lane, c);
+    uint32_t mine = 0, top = 0;  // lane k keeps the key and id of round k
+    int mine_id = 0;
+    for (int k = 0; k <= y; ++k) {
+      uint32_t m;
+      const int id = select_round<PL>(c, lane, &m);
+      if (k == 0) top = m;
+      if (lane == k) { mine = m; mine_id = id; }
+      wk.expert = id;
+    }
+    if (blockIdx.x == 0 && y == K - 1 && wave == 0) write_topk(mine, mine_id, top, K, lane, r.ids, r.wts);
+  }
+  const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
+  const int rbase = (blockIdx.x * 4 + wave) * RPW * RPI;
+  gateup_rows<QF, MOE_ACT_BF16, 1, 1, RPW>(a, wk, shared, rbase, lane >> lpr_log2, lane & (LPR - 1), lpr_log2,
+                                           [](int) { return 0; });
+}
+
 // One token: down projection of the shared expert and the K selected experts
 // for the block's RPI rows, combined in slot order:
 //   y[r] = o_shared[r] + sum_k w[k] o_k[r]   (the arithmetic of k_down + k_combine)
+// h holds the routed rows in slot order (row k: the expert of slot k), as
+// k_fused_gateup1 writes them.
 // The slots are split over the block's 4 waves (wave w takes slots w, w + 4,
 // ...; the shared expert is slot K), so that four waves per row group keep
 // the memory and the reductions busy; each wave reads its slots' weight rows
@@ -376,8 +413,7 @@ __global__ __launch_bounds__(256) void k_fused_down1(FfnArgs a, CombineArgs c, i
     const int slot = min(wave + 4 * j, nslots - 1);  // clamped: slots past the end are loaded but unused
     const bool sh = has_shared && slot == K;
     const int e = sh ? 0 : __builtin_amdgcn_readfirstlane(a.ids[slot]);
-    const int hrow = sh ? 0 : __builtin_amdgcn_readfirstlane(c.pair_pos[slot]);
-    hg[j].load_raw(sh ? a.hs : a.h, (size_t)hrow * I + (size_t)gc * kGroup);
+    hg[j].load_raw(sh ? a.hs : a.h, (size_t)(sh ? 0 : slot) * I + (size_t)gc * kGroup);
     tw[j].load(expert_view<QF>(sh ? a.sdown : a.down, e, a.H, I), rbase, rsub, RPI, a.H, sub, LPR);
   }
   // 2. o for each slot and row, into LDS
@@ -422,6 +458,17 @@ static hipError_t fused_gateup_pl(const RouterArgs& r, const PermuteArgs& pm, co
   const int rows_per_block = 4 * (a.T == 1 ? kFusedRpw1 : kRPW) * rpi;
   const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, a.T * a.K + (a.n_shared && a.hs ? 1 : 0));
   const int pl = regs_per_lane(a.E);
+  if (a.T == 1 && fused_down1_ok(1, a.K, a.I)) {  // h in slot order for k_fused_down1
+    auto go1 = [&](auto kern) { kern<<<grid, 256, 0, s>>>(r, a, lpr_log2); };
+    switch (pl) {
+      case 1: go1(k_fused_gateup1<QF, 1, kFusedRpw1>); break;
+      case 2: go1(k_fused_gateup1<QF, 2, kFusedRpw1>); break;
+      case 4: go1(k_fused_gateup1<QF, 4, kFusedRpw1>); break;
+      case 8: go1(k_fused_gateup1<QF, 8, kFusedRpw1>); break;
+      default: go1(k_fused_gateup1<QF, 16, kFusedRpw1>); break;
+    }
+    return hipGetLastError();
+  }
   auto go = [&](auto kern) { kern<<<grid, 256, 0, s>>>(r, pm, a, lpr_log2); };
   if (a.T == 1) {
     switch (pl) {
