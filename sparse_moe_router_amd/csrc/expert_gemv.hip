@@ -285,6 +285,8 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
 
 constexpr int kFusedMaxPairs = 128;
 constexpr int kFusedRpw1 = 2;  // rows per wave of the one-token fused gate/up
+constexpr int kDownRpw1 = 2;   // row groups per wave of the one-token down + combine
+constexpr int kFusedMaxK1 = 16;  // top-K of the one-token path
 
 // gate/up with the top-K and the stable token -> expert ordering recomputed in
 // every block from the router logits (2 KiB per token at E = 512): block row y
@@ -350,13 +352,17 @@ k_fused_gateup(RouterArgs r, PermuteArgs pm, FfnArgs a, int lpr_log2) {
 
 // One token: block row k < K computes the expert picked in selection round k
 // and writes h row k (h in slot order, as k_fused_down1 reads it); row K is
-// the shared expert.  Each wave runs the selection itself and stops after
-// round k, so the rows of the first picks stream their weights while the
-// later picks are still being selected.  The block at (0, K - 1) runs every
-// round and writes ids and weights as moe_router_topk does.
+// the shared expert.  Wave 0 of a block runs the selection and stops after
+// round k (one selecting wave per block: every block of the row repeats the
+// same selection, so it is kept off the other waves' SIMDs, and at raised
+// priority, ahead of other blocks' dequantisation), so the rows of the first
+// picks stream their weights while the later picks are still being selected.
+// The block at (0, K - 1) runs every round and writes ids and weights as
+// moe_router_topk does.
 template <int QF, int PL, int RPW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MOE_ACT_BF16, 1, 1)))) void
 k_fused_gateup1(RouterArgs r, FfnArgs a, int lpr_log2) {
+  __shared__ int32_t s_pick[64];  // expert id of each selection round
   const int K = a.K;
   const int y = blockIdx.y;
   const bool shared = y == K;
@@ -364,18 +370,27 @@ k_fused_gateup1(RouterArgs r, FfnArgs a, int lpr_log2) {
   Work wk;
   wk.lo = shared ? 0 : y; wk.n = 1; wk.pair0 = y; wk.expert = -1;
   if (!shared) {
-    uint64_t c[PL];
-    lane_candidates<PL>(r.logits, r.E, lane, c);
-    uint32_t mine = 0, top = 0;  // lane k keeps the key and id of round k
-    int mine_id = 0;
-    for (int k = 0; k <= y; ++k) {
-      uint32_t m;
-      const int id = select_round<PL>(c, lane, &m);
-      if (k == 0) top = m;
-      if (lane == k) { mine = m; mine_id = id; }
-      wk.expert = id;
+    if (wave == 0) {
+      __builtin_amdgcn_s_setprio(3);
+      LaneSorted<PL> ls;
+      ls.load(r.logits, r.E, lane);
+      uint32_t mine = 0, top = 0;  // lane k keeps the key of round k
+#pragma unroll
+      for (int k = 0; k < kFusedMaxK1; ++k) {  // unrolled: the candidate registers stay in place
+        if (k <= y) {
+          const uint32_t m = ls.round(lane, k, s_pick);
+          if (k == 0) top = m;
+          if (lane == k) mine = m;
+        }
+      }
+      if (blockIdx.x == 0 && y == K - 1) {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        write_topk(mine, s_pick[min(lane, K - 1)], top, K, lane, r.ids, r.wts);
+      }
+      __builtin_amdgcn_s_setprio(0);
     }
-    if (blockIdx.x == 0 && y == K - 1 && wave == 0) write_topk(mine, mine_id, top, K, lane, r.ids, r.wts);
+    __syncthreads();
+    wk.expert = __builtin_amdgcn_readfirstlane(s_pick[y]);
   }
   const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
   const int rbase = (blockIdx.x * 4 + wave) * RPW * RPI;
@@ -393,20 +408,21 @@ k_fused_gateup1(RouterArgs r, FfnArgs a, int lpr_log2) {
 // the memory and the reductions busy; each wave reads its slots' weight rows
 // and h groups directly, the products meet in LDS and wave 0 combines them.
 // The routing values are read with scalar loads.
-template <int QF, int SPW>
+template <int QF, int SPW, int RPW>
 __global__ __launch_bounds__(256) void k_fused_down1(FfnArgs a, CombineArgs c, int lpr_log2) {
-  __shared__ float s_o[4 * SPW][64];  // [slot][row of the block]
+  constexpr int kRows = 64 * RPW;                 // upper bound of RPW * RPI
+  __shared__ float s_o[4 * SPW][kRows];           // [slot][row of the block]
   const int K = a.K, I = a.I;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
   const int sub = lane & (LPR - 1), rsub = lane >> lpr_log2;
   const int G = I / kGroup;
-  const int rbase = blockIdx.x * RPI;
+  const int rbase = blockIdx.x * RPI * RPW;       // rows rbase + rsub + rr * RPI
   const bool has_shared = a.so != nullptr;  // the shared expert is present
   const int nslots = K + (has_shared ? 1 : 0);
   const int gc = min(sub, G - 1);
   // 1. this wave's slots: weight rows and the matching h groups, all requested first
-  RowTile<QF, 1, 1> tw[SPW];
+  RowTile<QF, RPW, 1> tw[SPW];
   XGroup<QF, MOE_ACT_BF16> hg[SPW];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
@@ -422,18 +438,22 @@ __global__ __launch_bounds__(256) void k_fused_down1(FfnArgs a, CombineArgs c, i
   for (int j = 0; j < SPW; ++j) {
     const int slot = wave + 4 * j;
     hg[j].prep();
-    const float v = group_acc<QF, MOE_ACT_BF16>(0.f, tw[j].c[0][0], tw[j].s[0][0], tw[j].m[0][0], hg[j]);
-    const float o = seg_sum(gok ? v : 0.f, LPR);
-    if (slot < nslots && sub == 0) s_o[slot][rsub] = o;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const float v = group_acc<QF, MOE_ACT_BF16>(0.f, tw[j].c[rr][0], tw[j].s[rr][0], tw[j].m[rr][0], hg[j]);
+      const float o = seg_sum(gok ? v : 0.f, LPR);
+      if (slot < nslots && sub == 0) s_o[slot][rr * RPI + rsub] = o;
+    }
   }
   __syncthreads();
-  // 3. the combine, in slot order (shared first), by lane r of wave 0 for row rbase + r
-  if (wave == 0 && lane < RPI) {
-    const int r = rbase + lane;
-    float acc = has_shared ? s_o[K][lane] : 0.f;
+  // 3. the combine, in slot order (shared first), one row per thread
+  const int nrows = RPW * RPI;
+  for (int i = threadIdx.x; i < nrows; i += 256) {
+    const int r = rbase + i;  // s_o row i is row rbase + rsub + rr * RPI with i = rr * RPI + rsub
+    float acc = has_shared ? s_o[K][i] : 0.f;
     for (int k = 0; k < K; ++k) {
       const float w = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.w[k])));
-      acc = fmaf(w, s_o[k][lane], acc);
+      acc = fmaf(w, s_o[k][i], acc);
     }
     if (r < a.H) {
       c.y[r] = acc;
@@ -447,7 +467,9 @@ bool fused_decode_ok(int T, int K, int E, int H, int I, int act) {
          I <= 64 * kGroup;
 }
 
-bool fused_down1_ok(int T, int K, int I) { return T == 1 && K <= 16 && I <= 64 * kGroup; }
+// One token through k_fused_gateup1 (selection state in LaneSorted: E <= 512)
+// and k_fused_down1, with h in slot order between them.
+bool fused_down1_ok(int T, int K, int E, int I) { return T == 1 && K <= kFusedMaxK1 && E <= 512 && I <= 64 * kGroup; }
 
 template <int QF>
 static hipError_t fused_gateup_pl(const RouterArgs& r, const PermuteArgs& pm, const FfnArgs& a, hipStream_t s) {
@@ -458,14 +480,13 @@ static hipError_t fused_gateup_pl(const RouterArgs& r, const PermuteArgs& pm, co
   const int rows_per_block = 4 * (a.T == 1 ? kFusedRpw1 : kRPW) * rpi;
   const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, a.T * a.K + (a.n_shared && a.hs ? 1 : 0));
   const int pl = regs_per_lane(a.E);
-  if (a.T == 1 && fused_down1_ok(1, a.K, a.I)) {  // h in slot order for k_fused_down1
+  if (fused_down1_ok(a.T, a.K, a.E, a.I)) {  // h in slot order for k_fused_down1
     auto go1 = [&](auto kern) { kern<<<grid, 256, 0, s>>>(r, a, lpr_log2); };
     switch (pl) {
       case 1: go1(k_fused_gateup1<QF, 1, kFusedRpw1>); break;
       case 2: go1(k_fused_gateup1<QF, 2, kFusedRpw1>); break;
       case 4: go1(k_fused_gateup1<QF, 4, kFusedRpw1>); break;
-      case 8: go1(k_fused_gateup1<QF, 8, kFusedRpw1>); break;
-      default: go1(k_fused_gateup1<QF, 16, kFusedRpw1>); break;
+      default: go1(k_fused_gateup1<QF, 8, kFusedRpw1>); break;
     }
     return hipGetLastError();
   }
@@ -501,12 +522,12 @@ static hipError_t fused_down1_q(const FfnArgs& a, const CombineArgs& c, hipStrea
   int lpr_log2, gpl;
   lane_split(a.I, &lpr_log2, &gpl);
   const int rpi = 64 >> lpr_log2;
-  const dim3 grid((a.H + rpi - 1) / rpi);
+  const dim3 grid((a.H + rpi * kDownRpw1 - 1) / (rpi * kDownRpw1));
   const int nslots = a.K + (a.so ? 1 : 0);
-  if (nslots <= 4) k_fused_down1<QF, 1><<<grid, 256, 0, s>>>(a, c, lpr_log2);
-  else if (nslots <= 8) k_fused_down1<QF, 2><<<grid, 256, 0, s>>>(a, c, lpr_log2);
-  else if (nslots <= 12) k_fused_down1<QF, 3><<<grid, 256, 0, s>>>(a, c, lpr_log2);
-  else k_fused_down1<QF, 5><<<grid, 256, 0, s>>>(a, c, lpr_log2);
+  if (nslots <= 4) k_fused_down1<QF, 1, kDownRpw1><<<grid, 256, 0, s>>>(a, c, lpr_log2);
+  else if (nslots <= 8) k_fused_down1<QF, 2, kDownRpw1><<<grid, 256, 0, s>>>(a, c, lpr_log2);
+  else if (nslots <= 12) k_fused_down1<QF, 3, kDownRpw1><<<grid, 256, 0, s>>>(a, c, lpr_log2);
+  else k_fused_down1<QF, 5, kDownRpw1><<<grid, 256, 0, s>>>(a, c, lpr_log2);
   return hipGetLastError();
 }
 

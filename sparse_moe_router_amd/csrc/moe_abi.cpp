@@ -136,7 +136,7 @@ moe_status layer_forward_impl(const moe_layer& L, const void* x, int32_t T, floa
   if (fused_decode_ok(T, L.top_k, L.n_experts, L.hidden, L.inter, L.act)) {
     // few tokens: routing recomputed inside the gate/up kernel; one token: down + combine fused
     MOE_TRY(dev(launch_fused_gateup(ra, pa, fa, s)));
-    if (fused_down1_ok(T, L.top_k, L.inter)) return dev(launch_fused_down1(fa, ca, s));
+    if (fused_down1_ok(T, L.top_k, L.n_experts, L.inter)) return dev(launch_fused_down1(fa, ca, s));
     MOE_TRY(dev(launch_down(fa, s)));
     return dev(launch_combine(ca, s));
   }

@@ -82,6 +82,18 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(a, b);
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u<kDppXor1>(v));
+  v = min(v, dpp_u<kDppXor2>(v));
+  v = min(v, dpp_u<kDppHalfMirror>(v));
+  v = min(v, dpp_u<kDppMirror>(v));
+  uint32_t a, b;
+  swap16(v, &a, &b);
+  v = min(a, b);
+  swap32(v, &a, &b);
+  return min(a, b);
+}
+
 __device__ __forceinline__ int wave_min_i32(int v) {
   v = min(v, (int)dpp_u<kDppXor1>((uint32_t)v));
   v = min(v, (int)dpp_u<kDppXor2>((uint32_t)v));

@@ -118,6 +118,83 @@ __device__ __forceinline__ void wave_topk_regs(const float* lg, int E, int K, in
   }
 }
 
+// Selection state of one wave for E <= 64 PL experts (PL <= 8): lane l holds
+// the logits of the consecutive experts PL l + i (i < PL) as 32-bit keys sorted
+// in descending order (larger logit first, then lower expert id; 0 = empty),
+// with each key's position i in a 4-bit field of pos (field j: the lane's j-th
+// key).  Since a lower lane holds lower ids, the lowest lane among lanes whose
+// heads tie holds the lowest id, so a round needs one wave maximum and one
+// ballot; the picks come out in the same order as from wave_topk_regs.
+template <int PL>
+struct LaneSorted {
+  static_assert(PL <= 8, "positions are packed in one 32-bit register");
+  uint32_t k[PL];
+  uint32_t pos;
+
+  // lg: 16-byte aligned when E == 64 PL (the lane's PL logits are then read
+  // as 16-byte vectors)
+  __device__ __forceinline__ void load(const float* lg, int E, int lane) {
+    float v[PL];
+    if (PL >= 4 && E == 64 * PL) {
+#pragma unroll
+      for (int q = 0; q < PL / 4; ++q) {
+        const float4 f = reinterpret_cast<const float4*>(lg + PL * lane)[q];
+        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) v[i] = lg[min(PL * lane + i, E - 1)];  // clamped: no conditional loads
+    }
+    uint64_t c[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = PL * lane + i;
+      c[i] = e < E ? sel_key(v[i], e) : 0ull;
+    }
+    auto cx = [&](int a, int b) {  // c[a] >= c[b] afterwards
+      const uint64_t hi = c[a] > c[b] ? c[a] : c[b];
+      const uint64_t lo = c[a] > c[b] ? c[b] : c[a];
+      c[a] = hi;
+      c[b] = lo;
+    };
+    if constexpr (PL == 2) {
+      cx(0, 1);
+    } else if constexpr (PL == 4) {
+      cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+    } else if constexpr (PL == 8) {  // 19 comparators, depth 6
+      cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
+      cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
+      cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
+      cx(2, 4); cx(3, 5);
+      cx(1, 4); cx(3, 6);
+      cx(1, 2); cx(3, 4); cx(5, 6);
+    }
+    pos = 0;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      k[i] = (uint32_t)(c[i] >> 32);
+      pos |= ((uint32_t)(key_id(c[i]) - PL * lane) & 15u) << (4 * i);
+    }
+  }
+
+  // One round: the largest remaining key of the wave (returned, uniform); the
+  // lowest lane holding it (the lowest id) drops it and writes its expert id
+  // to ids_lds[round].  The winner is found from the ballot with mbcnt, so the
+  // round has no scalar step between the maximum and the shift.
+  __device__ __forceinline__ uint32_t round(int lane, int rnd, int32_t* ids_lds) {
+    const uint32_t m = wave_max_u32(k[0]);
+    const uint64_t tied = __ballot(k[0] == m);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(tied >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)tied, 0u));
+    const bool win = k[0] == m && below == 0;
+    if (win) ids_lds[rnd] = PL * lane + (int)(pos & 15u);
+#pragma unroll
+    for (int i = 0; i + 1 < PL; ++i) k[i] = win ? k[i + 1] : k[i];  // selects, not a branch
+    k[PL - 1] = win ? 0u : k[PL - 1];
+    pos = win ? pos >> 4 : pos;
+    return m;
+  }
+};
+
 // logits per lane held in registers for E experts: 1, 2, 4, 8 or 16
 inline int regs_per_lane(int E) {
   int pl = 1;
