@@ -28,6 +28,25 @@ import numpy as np
 
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of the roofline kernel (k_gateup, one token, 10 experts +
+# shared) from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) over this
+# script, each scaled by what the counter reads for a 256 MiB device copy
+# (FETCH_SIZE x 1.99978, WRITE_SIZE x 1.0).  Valid for the kernel sources whose
+# fingerprint is stored; reported as null once they change.
+TRAFFIC_SOURCES = ("expert_gemv.hip", "gemv_tile.h", "moe_device.h", "topk.h", "moe_internal.h")
+MEASURED_TRAFFIC = {"bytes_per_launch": 19673311,
+                    "sources_sha256": "729cd7ebe060baa1d45ce45d6357d291823b4c9fd8748b5f6b13e9c41d7057c1"}
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    d = hashlib.sha256()
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_router_amd", "csrc")
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(root, name), "rb") as f:
+            d.update(f.read())
+    return d.hexdigest()
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -43,6 +62,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 4096-token prefill figure")
     ap.add_argument("--prefill-steps", type=int, default=16)
     ap.add_argument("--kernel-reps", type=int, default=2000)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run 4 device-to-device copies of this many MiB (a counter calibration "
+                         "kernel of known size for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -168,6 +190,19 @@ def main():
         extra["prefill_frac_of_bf16_mfma"] = flops / (pms * 1e-3) / 2.5e15
         log(f"prefill: {pms:.3f} ms/layer, {extra['prefill_tok_s']:.0f} tok/s")
 
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: 4 copies of {args.copy_calib_mib} MiB")
+
+    traffic = (MEASURED_TRAFFIC["bytes_per_launch"]
+               if MEASURED_TRAFFIC["sources_sha256"] == kernel_sources_sha256() else None)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(spec, ld0)
@@ -194,7 +229,7 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "expert gate/up + SwiGLU (k_gateup)",
             "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-            "traffic": None, "us_per_launch": k_us, "algorithmic_bytes_per_launch": gu_bytes,
+            "traffic": traffic, "us_per_launch": k_us, "algorithmic_bytes_per_launch": gu_bytes,
         },
         "cpu_baseline": cpu,
         "extra": extra,

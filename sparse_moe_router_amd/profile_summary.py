@@ -1,9 +1,15 @@
-"""Condense a rocprofv3 kernel-stats CSV (--stats --output-format csv) into a
-short text table: kernel, calls, average / min / max duration, share."""
+"""Condense rocprofv3 CSV output into short text tables.
+
+  python -m sparse_moe_router_amd.profile_summary stats  <kernel_stats.csv>
+      kernel, calls, average / min / max duration, share (--kernel-trace --stats)
+  python -m sparse_moe_router_amd.profile_summary counters <counter_collection.csv> [name-substring ...]
+      per kernel: dispatches and the mean value of each counter per dispatch (--pmc)
+"""
 from __future__ import annotations
 
 import csv
 import sys
+from collections import defaultdict
 
 
 def summarize(path: str, top: int = 25) -> str:
@@ -15,5 +21,32 @@ def summarize(path: str, top: int = 25) -> str:
     return "\n".join(out)
 
 
+def counter_means(path: str, names=()) -> dict:
+    """{(kernel, counter): (dispatches, mean value per dispatch)} for kernels whose name contains any of `names`
+    (all kernels if none are given)."""
+    acc = defaultdict(lambda: [0, 0.0])
+    seen = defaultdict(set)
+    for r in csv.DictReader(open(path)):
+        k = r["Kernel_Name"]
+        if names and not any(n in k for n in names):
+            continue
+        key = (k, r["Counter_Name"])
+        acc[key][1] += float(r["Counter_Value"])
+        seen[key].add(r["Dispatch_Id"])
+    return {key: (len(seen[key]), v[1] / max(len(seen[key]), 1)) for key, v in acc.items()}
+
+
+def counters(path: str, names=()) -> str:
+    out = [f"{'kernel':<72} {'counter':<12} {'dispatches':>10} {'mean/dispatch':>14}"]
+    for (k, c), (n, mean) in sorted(counter_means(path, names).items()):
+        out.append(f"{k[:72]:<72} {c:<12} {n:>10} {mean:>14.1f}")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    print(summarize(sys.argv[1]))
+    if len(sys.argv) >= 3 and sys.argv[1] == "counters":
+        print(counters(sys.argv[2], tuple(sys.argv[3:])))
+    elif len(sys.argv) >= 3 and sys.argv[1] == "stats":
+        print(summarize(sys.argv[2]))
+    else:
+        print(summarize(sys.argv[1]))
