@@ -145,6 +145,153 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_s
   }
 }
 
+// ---- one token, H <= 2048 (one 32-element group per lane) ----------------
+
+constexpr int kFusedRpw1 = 2;  // rows per wave of the one-token gate/up kernels
+
+// The token's activations staged once per block in LDS, prepared for
+// group_acc: group g's 16 words of pairs in q[0..3][g], its offset term in
+// c[g] (lane-contiguous: every read below is conflict-free).
+struct XLds {
+  uint4 q[4][64];
+  float c[64];
+};
+
+// One wave stages x (lane = group; groups past H / 32 repeat the last one).
+template <int QF>
+__device__ __forceinline__ void stage_x1(const void* x, int H, int lane, XLds& xs) {
+  XGroup<QF, MOE_ACT_BF16> xg;
+  xg.load_raw(x, (size_t)min(lane, H / kGroup - 1) * kGroup);
+  xg.prep();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xs.q[i][lane] = make_uint4(xg.p[4 * i], xg.p[4 * i + 1], xg.p[4 * i + 2], xg.p[4 * i + 3]);
+  xs.c[lane] = xg.c;
+}
+
+template <int QF>
+__device__ __forceinline__ void read_x1(const XLds& xs, int lane, XGroup<QF, MOE_ACT_BF16>& xg) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = xs.q[i][lane];
+    xg.p[4 * i] = v.x; xg.p[4 * i + 1] = v.y; xg.p[4 * i + 2] = v.z; xg.p[4 * i + 3] = v.w;
+  }
+  xg.c = xs.c[lane];
+  xg.sx = xg.c;
+}
+
+// The 2 RPW per-lane partial sums of a wave (gate rows 0..RPW-1, then up
+// rows) reduced over the 64 lanes together: a permlane32 swap pairs gate row
+// i with up row i (lanes < 32 keep the gate sum), a permlane16 swap halves
+// the values again, one DPP rotate by 8 when RPW = 4, then DPP steps within
+// the remaining 16 or 8 lanes.  Afterwards lane (32 / RPW) i (i < RPW) holds
+// gate row i in *g and up row i in *u.
+template <int RPW>
+__device__ __forceinline__ void reduce_gu1(const float (&v)[2 * RPW], int lane, float* g, float* u) {
+  static_assert(RPW == 1 || RPW == 2 || RPW == 4, "one, two or four rows per wave");
+  auto f = [](uint32_t b) { return __uint_as_float(b); };
+  auto b = [](float x) { return __float_as_uint(x); };
+  if constexpr (RPW == 1) {
+    const auto r0 = __builtin_amdgcn_permlane32_swap(b(v[0]), b(v[1]), false, false);
+    float sum = f(r0[0]) + f(r0[1]);  // lanes < 32: gate, >= 32: up
+    const auto r1 = __builtin_amdgcn_permlane16_swap(b(sum), b(sum), false, false);
+    sum = f(r1[0]) + f(r1[1]);
+    sum += dpp_f<kDppXor1>(sum);
+    sum += dpp_f<kDppXor2>(sum);
+    sum += dpp_f<kDppHalfMirror>(sum);
+    sum += dpp_f<kDppMirror>(sum);
+    const auto r = __builtin_amdgcn_permlane32_swap(b(sum), b(sum), false, false);
+    *g = f(r[0]);
+    *u = f(r[1]);
+    return;
+  }
+  float w[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(b(v[i]), b(v[i + RPW]), false, false);
+    w[i] = f(r[0]) + f(r[1]);
+  }
+  float x[RPW / 2 + (RPW == 1)];
+#pragma unroll
+  for (int i = 0; i < RPW / 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(b(w[i]), b(w[i + RPW / 2]), false, false);
+    x[i] = f(r[0]) + f(r[1]);
+  }
+  float sum;
+  if constexpr (RPW == 4) {
+    const bool hi = (lane & 8) != 0;
+    const float keep = hi ? x[1] : x[0], give = hi ? x[0] : x[1];
+    sum = keep + dpp_f<kDppRor8>(give);
+    sum += dpp_f<kDppXor1>(sum);
+    sum += dpp_f<kDppXor2>(sum);
+    sum += dpp_f<kDppHalfMirror>(sum);
+  } else {
+    sum = x[0];
+    sum += dpp_f<kDppXor1>(sum);
+    sum += dpp_f<kDppXor2>(sum);
+    sum += dpp_f<kDppHalfMirror>(sum);
+    sum += dpp_f<kDppMirror>(sum);
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(b(sum), b(sum), false, false);  // gate half | up half
+  *g = f(r[0]);
+  *u = f(r[1]);
+}
+
+// gate/up + SwiGLU of RPW rows (rbase ..) of one expert for one token, with
+// the weight rows already requested and x in LDS; h row hrow.
+template <int QF, int RPW>
+__device__ __forceinline__ void gateup_rows1(const FfnArgs& a, bool shared, int hrow, int rbase, int lane,
+                                             const RowTile<QF, RPW, 1>& tg, const RowTile<QF, RPW, 1>& tu,
+                                             const XLds& xs) {
+  XGroup<QF, MOE_ACT_BF16> xg;
+  read_x1<QF>(xs, lane, xg);
+  const bool gok = lane < a.H / kGroup;
+  float v[2 * RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    __builtin_amdgcn_sched_barrier(0);  // one row at a time: unpacked codes stay few
+    const float gv = group_acc<QF, MOE_ACT_BF16>(0.f, tg.c[rr][0], tg.s[rr][0], tg.m[rr][0], xg);
+    const float uv = group_acc<QF, MOE_ACT_BF16>(0.f, tu.c[rr][0], tu.s[rr][0], tu.m[rr][0], xg);
+    v[rr] = gok ? gv : 0.f;
+    v[RPW + rr] = gok ? uv : 0.f;
+  }
+  float g, u;
+  reduce_gu1<RPW>(v, lane, &g, &u);
+  constexpr int kStride = RPW == 1 ? 32 : 32 / RPW;
+  const int rr = lane / kStride, r = rbase + rr;
+  if (lane < 32 && (lane & (kStride - 1)) == 0 && r < a.I)
+    store_act<MOE_ACT_BF16>(shared ? a.hs : a.h, (size_t)hrow * a.I + r, silu(g) * u);
+}
+
+// Standalone gate/up for one token (moe_expert_gate_up_q, T = 1): block row
+// k < K computes pair k, whose expert is ids[k], into h row pair_pos[k] (the
+// rank of (ids[k], k)), both from one load of the K ids; row K is the shared
+// expert.  Wave 0 stages x in LDS while the weights are in flight.
+template <int QF, int RPW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MOE_ACT_BF16, 1, 1)))) void
+k_gateup1(FfnArgs a) {
+  __shared__ XLds xs;
+  const int K = a.K, y = blockIdx.y;
+  const bool shared = y == K;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int e = 0, hrow = 0;
+  if (!shared) {
+    const int id = a.ids[min(lane, K - 1)];
+    e = __builtin_amdgcn_readlane(id, y);
+    hrow = __popcll(__ballot(lane < K && (id < e || (id == e && lane < y))));
+  }
+  const int rbase = (blockIdx.x * 4 + wave) * RPW;
+  RowTile<QF, RPW, 1> tg, tu;
+  tg.load(expert_view<QF>(shared ? a.sgate : a.gate, e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+  tu.load(expert_view<QF>(shared ? a.sup : a.up, e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+  if (wave == 0) stage_x1<QF>(a.x, a.H, lane, xs);
+  __syncthreads();
+  gateup_rows1<QF, RPW>(a, shared, hrow, rbase, lane, tg, tu, xs);
+}
+
+bool gateup1_ok(const FfnArgs& a) {
+  return a.T == 1 && a.act == MOE_ACT_BF16 && a.H <= 64 * kGroup && a.K <= 64;
+}
+
 // down projection:  o[j][r] = Wd[r] . h_j   (fp32 out); h rows of an expert are
 // contiguous in sorted order, so no index is loaded before the weights.
 template <int QF, int ACT, int NT, int GPL, int RPW>
@@ -265,9 +412,22 @@ static hipError_t dispatch_act(const FfnArgs& a, bool gateup, hipStream_t s) {
   return dispatch_gpl<QF, MOE_ACT_BF16, 4>(a, gateup, s);
 }
 
+// rows per wave of the standalone one-token gate/up: the same as the fused
+// kernel's, so that both reduce in the same order and give the same bits
+constexpr int kGateup1Rpw = kFusedRpw1;
+
+template <int QF>
+static hipError_t gateup1_q(const FfnArgs& a, hipStream_t s) {
+  const dim3 grid((a.I + 4 * kGateup1Rpw - 1) / (4 * kGateup1Rpw), a.K + (a.n_shared && a.hs ? 1 : 0));
+  k_gateup1<QF, kGateup1Rpw><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (mfma_ok(a)) return launch_mfma_gateup(a, s);
+  if (gateup1_ok(a))
+    return a.qfmt == MOE_Q4_SYM_G32 ? gateup1_q<MOE_Q4_SYM_G32>(a, s) : gateup1_q<MOE_Q2_ASYM_G32>(a, s);
   return a.qfmt == MOE_Q4_SYM_G32 ? dispatch_act<MOE_Q4_SYM_G32>(a, true, s) : dispatch_act<MOE_Q2_ASYM_G32>(a, true, s);
 }
 
@@ -284,7 +444,6 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
 // (one token) down projection with the weighted combine.
 
 constexpr int kFusedMaxPairs = 128;
-constexpr int kFusedRpw1 = 2;  // rows per wave of the one-token fused gate/up
 constexpr int kDownRpw1 = 2;   // row groups per wave of the one-token down + combine
 constexpr int kFusedMaxK1 = 16;  // top-K of the one-token path
 
@@ -356,46 +515,51 @@ k_fused_gateup(RouterArgs r, PermuteArgs pm, FfnArgs a, int lpr_log2) {
 // round k (one selecting wave per block: every block of the row repeats the
 // same selection, so it is kept off the other waves' SIMDs, and at raised
 // priority, ahead of other blocks' dequantisation), so the rows of the first
-// picks stream their weights while the later picks are still being selected.
-// The block at (0, K - 1) runs every round and writes ids and weights as
-// moe_router_topk does.
+// picks stream their weights while the later picks are still being selected;
+// wave 1 meanwhile stages x in LDS.  The block at (0, K - 1) runs every round
+// and writes ids and weights as moe_router_topk does.
 template <int QF, int PL, int RPW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MOE_ACT_BF16, 1, 1)))) void
-k_fused_gateup1(RouterArgs r, FfnArgs a, int lpr_log2) {
+k_fused_gateup1(RouterArgs r, FfnArgs a) {
   __shared__ int32_t s_pick[64];  // expert id of each selection round
+  __shared__ XLds xs;
   const int K = a.K;
   const int y = blockIdx.y;
   const bool shared = y == K;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  Work wk;
-  wk.lo = shared ? 0 : y; wk.n = 1; wk.pair0 = y; wk.expert = -1;
-  if (!shared) {
-    if (wave == 0) {
-      __builtin_amdgcn_s_setprio(3);
-      LaneSorted<PL> ls;
-      ls.load(r.logits, r.E, lane);
-      uint32_t mine = 0, top = 0;  // lane k keeps the key of round k
-#pragma unroll
-      for (int k = 0; k < kFusedMaxK1; ++k) {  // unrolled: the candidate registers stay in place
-        if (k <= y) {
-          const uint32_t m = ls.round(lane, k, s_pick);
-          if (k == 0) top = m;
-          if (lane == k) mine = m;
-        }
-      }
-      if (blockIdx.x == 0 && y == K - 1) {
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        write_topk(mine, s_pick[min(lane, K - 1)], top, K, lane, r.ids, r.wts);
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
-    __syncthreads();
-    wk.expert = __builtin_amdgcn_readfirstlane(s_pick[y]);
+  const int rbase = (blockIdx.x * 4 + wave) * RPW;
+  RowTile<QF, RPW, 1> tg, tu;
+  if (shared) {  // no selection: the weights go out first
+    tg.load(expert_view<QF>(a.sgate, 0, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+    tu.load(expert_view<QF>(a.sup, 0, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
   }
-  const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
-  const int rbase = (blockIdx.x * 4 + wave) * RPW * RPI;
-  gateup_rows<QF, MOE_ACT_BF16, 1, 1, RPW>(a, wk, shared, rbase, lane >> lpr_log2, lane & (LPR - 1), lpr_log2,
-                                           [](int) { return 0; });
+  if (wave == 1) stage_x1<QF>(a.x, a.H, lane, xs);
+  if (!shared && wave == 0) {
+    __builtin_amdgcn_s_setprio(3);
+    LaneSorted<PL> ls;
+    ls.load(r.logits, r.E, lane);
+    uint32_t mine = 0, top = 0;  // lane k keeps the key of round k
+#pragma unroll
+    for (int k = 0; k < kFusedMaxK1; ++k) {  // unrolled: the candidate registers stay in place
+      if (k <= y) {
+        const uint32_t m = ls.round(lane, k, s_pick);
+        if (k == 0) top = m;
+        if (lane == k) mine = m;
+      }
+    }
+    if (blockIdx.x == 0 && y == K - 1) {
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      write_topk(mine, s_pick[min(lane, K - 1)], top, K, lane, r.ids, r.wts);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
+  __syncthreads();
+  if (!shared) {
+    const int e = __builtin_amdgcn_readfirstlane(s_pick[y]);
+    tg.load(expert_view<QF>(a.gate, e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+    tu.load(expert_view<QF>(a.up, e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+  }
+  gateup_rows1<QF, RPW>(a, shared, shared ? 0 : y, rbase, lane, tg, tu, xs);
 }
 
 // One token: down projection of the shared expert and the K selected experts
@@ -481,7 +645,9 @@ static hipError_t fused_gateup_pl(const RouterArgs& r, const PermuteArgs& pm, co
   const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, a.T * a.K + (a.n_shared && a.hs ? 1 : 0));
   const int pl = regs_per_lane(a.E);
   if (fused_down1_ok(a.T, a.K, a.E, a.I)) {  // h in slot order for k_fused_down1
-    auto go1 = [&](auto kern) { kern<<<grid, 256, 0, s>>>(r, a, lpr_log2); };
+    // one group of H per lane, kFusedRpw1 rows per wave
+    const dim3 grid1((a.I + 4 * kFusedRpw1 - 1) / (4 * kFusedRpw1), a.K + (a.n_shared && a.hs ? 1 : 0));
+    auto go1 = [&](auto kern) { kern<<<grid1, 256, 0, s>>>(r, a); };
     switch (pl) {
       case 1: go1(k_fused_gateup1<QF, 1, kFusedRpw1>); break;
       case 2: go1(k_fused_gateup1<QF, 2, kFusedRpw1>); break;

@@ -37,6 +37,7 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kDppRor8 = 0x128;       // lane i <- lane (i + 8) mod 16 within 16
 
 // {own value, value of the lane 16 (or 32) apart}, in some order
 __device__ __forceinline__ void swap16(uint32_t v, uint32_t* a, uint32_t* b) {
