@@ -431,9 +431,13 @@ hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
   return a.qfmt == MOE_Q4_SYM_G32 ? dispatch_act<MOE_Q4_SYM_G32>(a, true, s) : dispatch_act<MOE_Q2_ASYM_G32>(a, true, s);
 }
 
+template <int QF> static hipError_t down1_q(const FfnArgs& a, hipStream_t s);
+bool down1_ok(const FfnArgs& a);
+
 hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (mfma_ok(a)) return launch_mfma_down(a, s);
+  if (down1_ok(a)) return a.qfmt == MOE_Q4_SYM_G32 ? down1_q<MOE_Q4_SYM_G32>(a, s) : down1_q<MOE_Q2_ASYM_G32>(a, s);
   return a.qfmt == MOE_Q4_SYM_G32 ? dispatch_act<MOE_Q4_SYM_G32>(a, false, s) : dispatch_act<MOE_Q2_ASYM_G32>(a, false, s);
 }
 
@@ -444,7 +448,6 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
 // (one token) down projection with the weighted combine.
 
 constexpr int kFusedMaxPairs = 128;
-constexpr int kDownRpw1 = 2;   // row groups per wave of the one-token down + combine
 constexpr int kFusedMaxK1 = 16;  // top-K of the one-token path
 
 // gate/up with the top-K and the stable token -> expert ordering recomputed in
@@ -562,58 +565,132 @@ k_fused_gateup1(RouterArgs r, FfnArgs a) {
   gateup_rows1<QF, RPW>(a, shared, shared ? 0 : y, rbase, lane, tg, tu, xs);
 }
 
-// One token: down projection of the shared expert and the K selected experts
-// for the block's RPI rows, combined in slot order:
-//   y[r] = o_shared[r] + sum_k w[k] o_k[r]   (the arithmetic of k_down + k_combine)
-// h holds the routed rows in slot order (row k: the expert of slot k), as
-// k_fused_gateup1 writes them.
-// The slots are split over the block's 4 waves (wave w takes slots w, w + 4,
-// ...; the shared expert is slot K), so that four waves per row group keep
-// the memory and the reductions busy; each wave reads its slots' weight rows
-// and h groups directly, the products meet in LDS and wave 0 combines them.
-// The routing values are read with scalar loads.
-template <int QF, int SPW, int RPW>
-__global__ __launch_bounds__(256) void k_fused_down1(FfnArgs a, CombineArgs c, int lpr_log2) {
-  constexpr int kRows = 64 * RPW;                 // upper bound of RPW * RPI
-  __shared__ float s_o[4 * SPW][kRows];           // [slot][row of the block]
-  const int K = a.K, I = a.I;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int LPR = 1 << lpr_log2, RPI = 64 >> lpr_log2;
-  const int sub = lane & (LPR - 1), rsub = lane >> lpr_log2;
-  const int G = I / kGroup;
-  const int rbase = blockIdx.x * RPI * RPW;       // rows rbase + rsub + rr * RPI
-  const bool has_shared = a.so != nullptr;  // the shared expert is present
-  const int nslots = K + (has_shared ? 1 : 0);
-  const int gc = min(sub, G - 1);
-  // 1. this wave's slots: weight rows and the matching h groups, all requested first
-  RowTile<QF, RPW, 1> tw[SPW];
-  XGroup<QF, MOE_ACT_BF16> hg[SPW];
+// ---- one token, down projection -------------------------------------------
+// 8 lanes per row (8 rows per wave instruction), lane sub of a row owning the
+// groups sub + 8 j (j < GPL, GPL = ceil(I / 256)): no lane idles at I = 768.
+// Each wave works on SPW slots (slot = wave + NW js, NW waves per block; the
+// shared expert is slot K).  It stages the h of its own slots in its LDS region first (prepared
+// once per (slot, group) instead of once per row group), then reads the
+// weights' groups against it.  A slot's dot product is accumulated in the
+// lane over j, then reduced over the row's 8 lanes with three DPP steps.
+// The standalone and the fused kernels share this code, so their o values
+// are the same bits.
+constexpr int kDownLpr1 = 8;
+constexpr int kDown1MaxWaves = 16;  // waves per block: one per slot up to 16 slots
+
+// LDS words of one wave's staged h (16 words of pairs + the offset term per
+// (slot, group)), rounded up to 16 bytes; a block holds one per wave
+__host__ __device__ constexpr int down1_wave_words(int spw, int G) { return (17 * spw * G + 3) & ~3; }
+
+template <int QF, int SPW, int GPL>
+struct Down1Wave {
+  RowTile<QF, 1, GPL> tw[SPW];
+  uint4* q;   // this wave's staged h: q[(js * 4 + i) * G + g]
+  float* c;   //                       c[js * G + g]
+  int G;
+
+  // stage h rows hrow[js] (of hs when sh[js]) and request the weight rows of
+  // experts e[js]; the h loads go out first (they do not wait on the ids).
+  __device__ __forceinline__ void load(const FfnArgs& a, const int (&hrow)[SPW], const bool (&sh)[SPW],
+                                       const int (&e)[SPW], int rbase, int lane, uint32_t* lds) {
+    G = a.I / kGroup;
+    q = reinterpret_cast<uint4*>(lds);
+    c = reinterpret_cast<float*>(lds + 16 * SPW * G);
+    constexpr int kRounds = (SPW * 32 + 63) / 64;  // items per lane (G <= 32)
+    XGroup<QF, MOE_ACT_BF16> xg[kRounds];
 #pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int slot = min(wave + 4 * j, nslots - 1);  // clamped: slots past the end are loaded but unused
-    const bool sh = has_shared && slot == K;
-    const int e = sh ? 0 : __builtin_amdgcn_readfirstlane(a.ids[slot]);
-    hg[j].load_raw(sh ? a.hs : a.h, (size_t)(sh ? 0 : slot) * I + (size_t)gc * kGroup);
-    tw[j].load(expert_view<QF>(sh ? a.sdown : a.down, e, a.H, I), rbase, rsub, RPI, a.H, sub, LPR);
-  }
-  // 2. o for each slot and row, into LDS
-  const bool gok = sub < G;
+    for (int r = 0; r < kRounds; ++r) {
+      const int it = min(lane + 64 * r, SPW * G - 1);  // clamped: items past the end repeat the last
+      const int js = it / G, g = it - js * G;
+      // js is not uniform: pick the row by selects over the wave's slots
+      int row = hrow[0];
+      bool s0 = sh[0];
 #pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int slot = wave + 4 * j;
-    hg[j].prep();
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const float v = group_acc<QF, MOE_ACT_BF16>(0.f, tw[j].c[rr][0], tw[j].s[rr][0], tw[j].m[rr][0], hg[j]);
-      const float o = seg_sum(gok ? v : 0.f, LPR);
-      if (slot < nslots && sub == 0) s_o[slot][rr * RPI + rsub] = o;
+      for (int k = 1; k < SPW; ++k) { row = js == k ? hrow[k] : row; s0 = js == k ? sh[k] : s0; }
+      xg[r].load_raw(s0 ? a.hs : a.h, (size_t)row * a.I + (size_t)g * kGroup);
     }
+    const int rsub = lane >> 3, sub = lane & 7;
+#pragma unroll
+    for (int js = 0; js < SPW; ++js)
+      tw[js].load(expert_view<QF>(sh[js] ? a.sdown : a.down, e[js], a.H, a.I), rbase, rsub, kDownLpr1, a.H, sub,
+                  kDownLpr1);
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int it = lane + 64 * r;
+      xg[r].prep();
+      if (it < SPW * G) {
+        const int js = it / G, g = it - js * G;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          q[(js * 4 + i) * G + g] = make_uint4(xg[r].p[4 * i], xg[r].p[4 * i + 1], xg[r].p[4 * i + 2], xg[r].p[4 * i + 3]);
+        c[js * G + g] = xg[r].c;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+
+  // o of slot js for the lane's row (every lane of the row gets it)
+  __device__ __forceinline__ float dot(int js, int lane) const {
+    const int sub = lane & 7;
+    float acc = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < GPL; ++gi) {
+      const int g = min(sub + 8 * gi, G - 1);
+      XGroup<QF, MOE_ACT_BF16> xg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = q[(js * 4 + i) * G + g];
+        xg.p[4 * i] = v.x; xg.p[4 * i + 1] = v.y; xg.p[4 * i + 2] = v.z; xg.p[4 * i + 3] = v.w;
+      }
+      xg.c = c[js * G + g];
+      xg.sx = xg.c;
+      const float v = group_acc<QF, MOE_ACT_BF16>(acc, tw[js].c[0][gi], tw[js].s[0][gi], tw[js].m[0][gi], xg);
+      acc = sub + 8 * gi < G ? v : acc;
+    }
+    acc += dpp_f<kDppXor1>(acc);
+    acc += dpp_f<kDppXor2>(acc);
+    acc += dpp_f<kDppHalfMirror>(acc);
+    return acc;
+  }
+};
+
+// One token: down projection of the shared expert and the K selected experts
+// for the block's 8 rows, combined in slot order:
+//   y[r] = o_shared[r] + sum_k w[k] o_k[r]   (the arithmetic of k_down1 + k_combine)
+// h holds the routed rows in slot order (row k: the expert of slot k), as
+// k_fused_gateup1 writes them.  The slots are split over the block's waves;
+// the per-slot o values meet in LDS and 8 threads combine them.  The routing
+// values are read with scalar loads.
+template <int QF, int SPW, int GPL>
+__global__ __launch_bounds__(64 * kDown1MaxWaves) void k_fused_down1(FfnArgs a, CombineArgs c) {
+  const int NW = blockDim.x >> 6;  // slot = wave + NW js
+  extern __shared__ __align__(16) uint32_t lds_d1[];
+  __shared__ float s_o[kDown1MaxWaves * SPW][8];  // [slot][row of the block]
+  const int K = a.K;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rbase = blockIdx.x * 8;
+  const bool has_shared = a.so != nullptr;
+  const int nslots = K + (has_shared ? 1 : 0);
+  int hrow[SPW], e[SPW];
+  bool sh[SPW];
+#pragma unroll
+  for (int js = 0; js < SPW; ++js) {
+    const int slot = min(wave + NW * js, nslots - 1);  // clamped: slots past the end are computed but unused
+    sh[js] = has_shared && slot == K;
+    hrow[js] = sh[js] ? 0 : slot;
+    e[js] = sh[js] ? 0 : __builtin_amdgcn_readfirstlane(a.ids[min(slot, K - 1)]);
+  }
+  Down1Wave<QF, SPW, GPL> dw;
+  dw.load(a, hrow, sh, e, rbase, lane, lds_d1 + wave * down1_wave_words(SPW, a.I / kGroup));
+#pragma unroll
+  for (int js = 0; js < SPW; ++js) {
+    const int slot = wave + NW * js;
+    const float o = dw.dot(js, lane);
+    if (slot < nslots && (lane & 7) == 0) s_o[slot][lane >> 3] = o;
   }
   __syncthreads();
-  // 3. the combine, in slot order (shared first), one row per thread
-  const int nrows = RPW * RPI;
-  for (int i = threadIdx.x; i < nrows; i += 256) {
-    const int r = rbase + i;  // s_o row i is row rbase + rsub + rr * RPI with i = rr * RPI + rsub
+  if (threadIdx.x < 8) {
+    const int i = threadIdx.x, r = rbase + i;
     float acc = has_shared ? s_o[K][i] : 0.f;
     for (int k = 0; k < K; ++k) {
       const float w = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.w[k])));
@@ -626,6 +703,45 @@ __global__ __launch_bounds__(256) void k_fused_down1(FfnArgs a, CombineArgs c, i
   }
 }
 
+// Standalone down projection for one token (moe_expert_down_q, T = 1): wave
+// slots as above; pair k reads h row pair_pos[k] and writes o row pair_pos[k]
+// (the rank of (ids[k], k), from one load of the ids), the shared expert hs
+// and so.
+template <int QF, int SPW, int GPL>
+__global__ __launch_bounds__(64 * kDown1MaxWaves) void k_down1(FfnArgs a) {
+  const int NW = blockDim.x >> 6;  // slot = wave + NW js
+  extern __shared__ __align__(16) uint32_t lds_d1[];
+  const int K = a.K;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rbase = blockIdx.x * 8;
+  const bool has_shared = a.so != nullptr;
+  const int nslots = K + (has_shared ? 1 : 0);
+  const int id = a.ids[min(lane, K - 1)];
+  int hrow[SPW], e[SPW];
+  bool sh[SPW];
+#pragma unroll
+  for (int js = 0; js < SPW; ++js) {
+    const int slot = min(wave + NW * js, nslots - 1);
+    sh[js] = has_shared && slot == K;
+    const int ek = __builtin_amdgcn_readlane(id, min(slot, K - 1));
+    e[js] = sh[js] ? 0 : ek;
+    hrow[js] = sh[js] ? 0 : (int)__popcll(__ballot(lane < K && (id < ek || (id == ek && lane < slot))));
+  }
+  Down1Wave<QF, SPW, GPL> dw;
+  dw.load(a, hrow, sh, e, rbase, lane, lds_d1 + wave * down1_wave_words(SPW, a.I / kGroup));
+  const int r = rbase + (lane >> 3);
+#pragma unroll
+  for (int js = 0; js < SPW; ++js) {
+    const int slot = wave + NW * js;
+    const float o = dw.dot(js, lane);
+    if (slot < nslots && (lane & 7) == 0 && r < a.H) (sh[js] ? a.so : a.o)[(size_t)hrow[js] * a.H + r] = o;
+  }
+}
+
+bool down1_ok(const FfnArgs& a) {
+  return a.T == 1 && a.act == MOE_ACT_BF16 && a.I <= 32 * kGroup && a.K + 1 <= kDown1MaxWaves * 2;
+}
+
 bool fused_decode_ok(int T, int K, int E, int H, int I, int act) {
   return act == MOE_ACT_BF16 && T * K <= kFusedMaxPairs && K <= 64 && E <= 64 * kRegLogits && H <= 64 * kGroup &&
          I <= 64 * kGroup;
@@ -633,7 +749,7 @@ bool fused_decode_ok(int T, int K, int E, int H, int I, int act) {
 
 // One token through k_fused_gateup1 (selection state in LaneSorted: E <= 512)
 // and k_fused_down1, with h in slot order between them.
-bool fused_down1_ok(int T, int K, int E, int I) { return T == 1 && K <= kFusedMaxK1 && E <= 512 && I <= 64 * kGroup; }
+bool fused_down1_ok(int T, int K, int E, int I) { return T == 1 && K <= kFusedMaxK1 && E <= 512 && I <= 32 * kGroup; }
 
 template <int QF>
 static hipError_t fused_gateup_pl(const RouterArgs& r, const PermuteArgs& pm, const FfnArgs& a, hipStream_t s) {
@@ -683,17 +799,35 @@ hipError_t launch_fused_gateup(const RouterArgs& r, const PermuteArgs& pm, const
                                   : fused_gateup_pl<MOE_Q2_ASYM_G32>(r, pm, a, s);
 }
 
+// one wave per slot up to 16 slots (SPW = 1), else two slots per wave;
+// GPL groups per lane (<= 4)
+#define MOE_DOWN1_DISPATCH(KERN, ...)                                                         \
+  do {                                                                                        \
+    const int G_ = a.I / kGroup, gpl_ = (G_ + kDownLpr1 - 1) / kDownLpr1;                     \
+    const int nslots_ = a.K + (a.so ? 1 : 0);                                                 \
+    const int spw_ = nslots_ <= kDown1MaxWaves ? 1 : 2;                                       \
+    const int nw_ = (nslots_ + spw_ - 1) / spw_;                                              \
+    const dim3 grid_((a.H + 7) / 8);                                                          \
+    auto go_ = [&](auto kern, int spw) {                                                      \
+      kern<<<grid_, 64 * nw_, (size_t)nw_ * down1_wave_words(spw, G_) * 4, s>>>(__VA_ARGS__); \
+    };                                                                                        \
+    auto by_gpl_ = [&](auto k1, auto k2, auto k3, auto k4, int spw) {                         \
+      if (gpl_ <= 1) go_(k1, spw); else if (gpl_ == 2) go_(k2, spw);                          \
+      else if (gpl_ == 3) go_(k3, spw); else go_(k4, spw);                                    \
+    };                                                                                        \
+    if (spw_ == 1) by_gpl_(KERN<QF, 1, 1>, KERN<QF, 1, 2>, KERN<QF, 1, 3>, KERN<QF, 1, 4>, 1); \
+    else by_gpl_(KERN<QF, 2, 1>, KERN<QF, 2, 2>, KERN<QF, 2, 3>, KERN<QF, 2, 4>, 2);           \
+  } while (0)
+
 template <int QF>
 static hipError_t fused_down1_q(const FfnArgs& a, const CombineArgs& c, hipStream_t s) {
-  int lpr_log2, gpl;
-  lane_split(a.I, &lpr_log2, &gpl);
-  const int rpi = 64 >> lpr_log2;
-  const dim3 grid((a.H + rpi * kDownRpw1 - 1) / (rpi * kDownRpw1));
-  const int nslots = a.K + (a.so ? 1 : 0);
-  if (nslots <= 4) k_fused_down1<QF, 1, kDownRpw1><<<grid, 256, 0, s>>>(a, c, lpr_log2);
-  else if (nslots <= 8) k_fused_down1<QF, 2, kDownRpw1><<<grid, 256, 0, s>>>(a, c, lpr_log2);
-  else if (nslots <= 12) k_fused_down1<QF, 3, kDownRpw1><<<grid, 256, 0, s>>>(a, c, lpr_log2);
-  else k_fused_down1<QF, 5, kDownRpw1><<<grid, 256, 0, s>>>(a, c, lpr_log2);
+  MOE_DOWN1_DISPATCH(k_fused_down1, a, c);
+  return hipGetLastError();
+}
+
+template <int QF>
+static hipError_t down1_q(const FfnArgs& a, hipStream_t s) {
+  MOE_DOWN1_DISPATCH(k_down1, a);
   return hipGetLastError();
 }
 

@@ -88,7 +88,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 // K <= 64, E <= 1024, H, I <= 2048, bf16 activations
 bool fused_decode_ok(int T, int K, int E, int H, int I, int act);
 hipError_t launch_fused_gateup(const RouterArgs& r, const PermuteArgs& pm, const FfnArgs& a, hipStream_t s);
-// one token: down projection fused with the combine (K <= 16, E <= 512, I <= 2048);
+// one token: down projection fused with the combine (K <= 16, E <= 512, I <= 1024);
 // h in slot order, as the one-token fused gate/up writes it
 bool fused_down1_ok(int T, int K, int E, int I);
 hipError_t launch_fused_down1(const FfnArgs& a, const CombineArgs& c, hipStream_t s);
