@@ -12,9 +12,10 @@ Prints one JSON line (rank 0, N = 1):
   roofline     HBM roofline of the dominant kernel (expert gate/up + SwiGLU),
                algorithmic bytes per launch / HIP-event time per launch
   cpu_baseline the CPU oracle on a bounded sample of the same workload
-plus extra fields: expert-weight GB/s of the whole layer, prefill tokens/s.
+plus extra fields: expert-weight GB/s of the whole layer, the same decode steps
+and gate/up launches replayed from captured HIP graphs, prefill tokens/s.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-prefill]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-prefill] [--no-graph]
 """
 from __future__ import annotations
 
@@ -62,6 +63,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 4096-token prefill figure")
     ap.add_argument("--prefill-steps", type=int, default=16)
     ap.add_argument("--kernel-reps", type=int, default=2000)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra timing of the same steps replayed from captured HIP graphs")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run 4 device-to-device copies of this many MiB (a counter calibration "
                          "kernel of known size for rocprofv3 --pmc runs)")
@@ -110,22 +113,51 @@ def main():
     y = torch.empty((4096, H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i):
-        api.moe_layer_forward(layers[i % args.copies], xs[i % n_tok:i % n_tok + 1], 1, y, ws=ws, stream=stream)
+    def step(i, st):
+        api.moe_layer_forward(layers[i % args.copies], xs[i % n_tok:i % n_tok + 1], 1, y, ws=ws, stream=st)
 
     for i in range(args.warmup):
-        step(i)
+        step(i, stream)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # directly launched steps: three kernel launches per step from the host
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(args.warmup + i, stream)
     end.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    ms_per_step = ms / args.steps
-    tok_s = args.steps / (ms / 1e3)
+    ms_per_step = start.elapsed_time(end) / args.steps
+    tok_s = 1e3 / ms_per_step
     log(f"decode: {ms_per_step * 1e3:.2f} us/step, {tok_s:.0f} tok/s")
+
+    # extra: the same steps replayed from captured HIP graphs (a serving loop's
+    # way of launching a step), args.copies steps per graph, 8 graphs over
+    # different tokens, cycled
+    graph_us = None
+    if not args.no_graph:
+        g_steps, n_graphs = args.copies, 8
+        cap = torch.cuda.Stream()
+
+        def capture(first):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(g_steps):
+                    step(first + i, torch.cuda.current_stream())
+            return g
+
+        graphs = [capture(j * g_steps) for j in range(n_graphs)]
+        for g in graphs:  # warm replays
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // g_steps)
+        start.record(stream)
+        for r in range(reps):
+            graphs[r % n_graphs].replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        graph_us = start.elapsed_time(end) * 1e3 / (reps * g_steps)
+        log(f"decode, HIP graph replay: {graph_us:.2f} us/step")
 
     # routing of each copy for its first timed token: distinct experts per step
     wts = torch.empty((1, K), dtype=torch.float32, device=dev)
@@ -155,6 +187,22 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     k_us = start.elapsed_time(end) * 1e3 / args.kernel_reps
+    # the same launches replayed from a captured graph
+    k_graph_us = None
+    gg = torch.cuda.CUDAGraph() if not args.no_graph else None
+    if gg is not None:
+        with torch.cuda.graph(gg, stream=torch.cuda.Stream()):
+            for c in range(args.copies):
+                api.moe_expert_gate_up_q(layers[c], xs[c:c + 1], 1, idss[c], offs[c], sps[c], h, hs)
+        gg.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.kernel_reps // args.copies)
+        start.record(stream)
+        for r in range(reps):
+            gg.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        k_graph_us = start.elapsed_time(end) * 1e3 / (reps * args.copies)
     gu_bytes_unit = 2 * workload.matrix_bytes(spec.qfmt, I, H)       # gate + up of one expert
     gu_bytes = (u_mean + 1) * gu_bytes_unit + (u_mean + 1) * H * 2 + (K + 1) * I * 2  # + x reads, h writes
     achieved = gu_bytes / (k_us * 1e-6) / 1e9
@@ -167,6 +215,8 @@ def main():
         "expert_weight_frac_of_8TBps": exp_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "layer_algorithmic_GBps": layer_bytes / (ms_per_step * 1e-3) / 1e9,
         "layer_algorithmic_bytes": layer_bytes,
+        "decode_graph_replay_us_per_step": graph_us,
+        "gateup_graph_replay_us_per_launch": k_graph_us,
         "distinct_experts_per_token": u_mean,
         "weight_copies": args.copies,
     }

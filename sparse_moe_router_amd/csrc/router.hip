@@ -9,7 +9,8 @@ namespace moe {
 
 constexpr int kSmallRoutePairs = 256;
 
-// logits[t][e] = sum_i W[e][i] x[t][i] + b[e].  One wave per router row e,
+// logits[t][e] = sum_i W[e][i] x[t][i] + b[e].  One wave per router row e
+// (blocks of 4 waves, or of one wave for one token),
 // NCH chunks of 256 elements (one float4 per lane each; chunks past H load a
 // clamped in-range address and are zeroed).  For each pass of NT tokens the
 // activations and the row are all requested before the first multiply.
@@ -17,7 +18,7 @@ template <int ACT, int NT, int NCH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_router_logits(RouterArgs a) {
   typedef float f4v __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int e = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (e >= a.E) return;
   const float* wrow = a.w + (size_t)e * a.H;
   int col[NCH];
@@ -286,7 +287,9 @@ __global__ __launch_bounds__(256) void k_route_small(RouterArgs a, PermuteArgs p
 template <int ACT, int NT>
 static void router_nch(const RouterArgs& a, dim3 grid, hipStream_t s) {
   const int nch = (a.H + 255) / 256;
-  const dim3 block(256);
+  // one token: one wave per block, so that the E rows spread over every CU
+  const dim3 block(a.T == 1 ? 64 : 256);
+  if (a.T == 1) grid.x = a.E;
   if (nch <= 1) k_router_logits<ACT, NT, 1><<<grid, block, 0, s>>>(a);
   else if (nch <= 2) k_router_logits<ACT, NT, 2><<<grid, block, 0, s>>>(a);
   else if (nch <= 4) k_router_logits<ACT, NT, 4><<<grid, block, 0, s>>>(a);

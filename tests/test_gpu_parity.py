@@ -378,6 +378,36 @@ def test_decode_many_inputs(family1):
     assert worst <= TOL
 
 
+def test_decode_graph_replay(family1):
+    """Decode steps captured in a HIP graph (as a serving loop or bench.py runs them) and replayed four
+    times, with eager work of the same layer and a fill kernel between the replays: every replay gives the
+    eager result bit for bit."""
+    ld, L = family1
+    spec = synth.SPECS["decode"]
+    x = synth.gen_x(spec, tokens=4)
+    xd = gu.x_dev(x, spec.act)
+    ws = api.workspace(L, 1, gu.DEV)
+    y_eager = torch.zeros((3, spec.hidden), dtype=torch.float32, device=gu.DEV)
+    for t in range(3):
+        api.moe_layer_forward(L, xd[t:t + 1], 1, y_eager[t:t + 1], ws=ws)
+    torch.cuda.synchronize()
+    want = y_eager.cpu().numpy()
+    y = torch.zeros_like(y_eager)
+    scratch = torch.empty((1, spec.hidden), dtype=torch.float32, device=gu.DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for t in range(3):
+            api.moe_layer_forward(L, xd[t:t + 1], 1, y[t:t + 1], ws=ws)
+    for rep in range(4):
+        y.zero_()
+        g.replay()
+        api.moe_layer_forward(L, xd[3:4], 1, scratch, ws=ws)  # eager step between the replays
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        gu.say(f"graph replay {rep}: max|dy| = {np.abs(got - want).max():.1e}")
+        assert np.array_equal(got, want)
+
+
 def test_prefill_sampled(family1):
     ld, L = family1
     spec = synth.SPECS["prefill"]
