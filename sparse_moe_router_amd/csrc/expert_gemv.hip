@@ -666,11 +666,17 @@ __global__ __launch_bounds__(64 * kDown1MaxWaves) void k_fused_down1(FfnArgs a, 
   const int NW = blockDim.x >> 6;  // slot = wave + NW js
   extern __shared__ __align__(16) uint32_t lds_d1[];
   __shared__ float s_o[kDown1MaxWaves * SPW][8];  // [slot][row of the block]
+  __shared__ float s_w[kDown1MaxWaves * SPW];     // combine weights
   const int K = a.K;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rbase = blockIdx.x * 8;
   const bool has_shared = a.so != nullptr;
   const int nslots = K + (has_shared ? 1 : 0);
+  // the combine's inputs are requested now, not after the products
+  float resid = 0.f;
+  if (threadIdx.x < K) s_w[threadIdx.x] = c.w[threadIdx.x];
+  if (c.x_next && threadIdx.x < 8 && rbase + (int)threadIdx.x < a.H)
+    resid = load_act<MOE_ACT_BF16>(c.x_resid, rbase + threadIdx.x);
   int hrow[SPW], e[SPW];
   bool sh[SPW];
 #pragma unroll
@@ -692,13 +698,10 @@ __global__ __launch_bounds__(64 * kDown1MaxWaves) void k_fused_down1(FfnArgs a, 
   if (threadIdx.x < 8) {
     const int i = threadIdx.x, r = rbase + i;
     float acc = has_shared ? s_o[K][i] : 0.f;
-    for (int k = 0; k < K; ++k) {
-      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.w[k])));
-      acc = fmaf(w, s_o[k][i], acc);
-    }
+    for (int k = 0; k < K; ++k) acc = fmaf(s_w[k], s_o[k][i], acc);
     if (r < a.H) {
       c.y[r] = acc;
-      if (c.x_next) store_act<MOE_ACT_BF16>(c.x_next, r, load_act<MOE_ACT_BF16>(c.x_resid, r) + acc);
+      if (c.x_next) store_act<MOE_ACT_BF16>(c.x_next, r, resid + acc);
     }
   }
 }

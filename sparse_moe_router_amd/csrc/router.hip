@@ -21,6 +21,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int e = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (e >= a.E) return;
   const float* wrow = a.w + (size_t)e * a.H;
+  const float bias = a.b ? a.b[e] : 0.0f;  // requested first: not a round trip after the sum
   int col[NCH];
   bool ok[NCH];
 #pragma unroll
@@ -67,7 +68,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       acc[j] = wave_sum(s);
     }
     if (lane == 0) {
-      const float bias = a.b ? a.b[e] : 0.0f;
 #pragma unroll
       for (int j = 0; j < NT; ++j)
         if (t0 + j < a.T) a.logits[(size_t)(t0 + j) * a.E + e] = acc[j] + bias;
