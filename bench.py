@@ -29,14 +29,14 @@ import numpy as np
 
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per launch of the roofline kernel (k_gateup, one token, 10 experts +
+# HBM bytes per launch of the roofline kernel (k_gateup1, one token, 10 experts +
 # shared) from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) over this
 # script, each scaled by what the counter reads for a 256 MiB device copy
-# (FETCH_SIZE x 1.99978, WRITE_SIZE x 1.0).  Valid for the kernel sources whose
+# (FETCH_SIZE x 1.99981, WRITE_SIZE x 1.0).  Valid for the kernel sources whose
 # fingerprint is stored; reported as null once they change.
 TRAFFIC_SOURCES = ("expert_gemv.hip", "gemv_tile.h", "moe_device.h", "topk.h", "moe_internal.h")
-MEASURED_TRAFFIC = {"bytes_per_launch": 19673311,
-                    "sources_sha256": "729cd7ebe060baa1d45ce45d6357d291823b4c9fd8748b5f6b13e9c41d7057c1"}
+MEASURED_TRAFFIC = {"bytes_per_launch": 19603723,
+                    "sources_sha256": "2112a2e45d778451f5c98b17e421022c7f06de0ce67e2e5e6bf688bfc8cbaeef"}
 
 
 def kernel_sources_sha256() -> str:
@@ -277,7 +277,7 @@ def main():
             "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)",
         },
         "roofline": {
-            "bound": "hbm", "kernel": "expert gate/up + SwiGLU (k_gateup)",
+            "bound": "hbm", "kernel": "expert gate/up + SwiGLU, one token (k_gateup1)",
             "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic, "us_per_launch": k_us, "algorithmic_bytes_per_launch": gu_bytes,
         },
