@@ -25,6 +25,7 @@
 // consecutive codes and are unpacked into the pairs (k_j, k_{j+4}); the
 // activations are stored in LDS in that same pair order.
 #include "gemv_tile.h"
+#include <type_traits>
 
 namespace moe {
 
@@ -291,7 +292,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
       for (int nt = 0; nt < WN; ++nt) acc[mi][mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf) {
+  auto compute = [&](int buf, auto mta_c) {
+    constexpr int MTA = decltype(mta_c)::value;  // active 16-row M tiles
     uint2 sc4[NMAT][WN], mn4[NMAT][WN];
 #pragma unroll
     for (int mi = 0; mi < NMAT; ++mi)
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     };
     auto lds_group = [&](int j, GroupOps& g) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < MTA; ++mt) {
         const uint4 v = *reinterpret_cast<const uint4*>(&s_a[buf][(mt * 16 + ln) * kRowWords + j * 16 + lc * 4]);
         g.af[mt][0] = v.x; g.af[mt][1] = v.y; g.af[mt][2] = v.z; g.af[mt][3] = v.w;
         g.cf[mt] = *reinterpret_cast<const f32x4_t*>(&s_c[buf][j][mt * 16 + lc * 4]);
@@ -349,12 +351,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           scc = half_of(sc4[mi][nt], j);
           if constexpr (QF == MOE_Q2_ASYM_G32) mnc = half_of(mn4[mi][nt], j) * -0.25f;
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) dc[mt] = mfma16(af[mt], bf, cf[mt]);
+          for (int mt = 0; mt < MTA; ++mt) dc[mt] = mfma16(af[mt], bf, cf[mt]);
         }
         if (p > 0) {
           const int mi = (p - 1) / WN, nt = (p - 1) % WN;
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
+          for (int mt = 0; mt < MTA; ++mt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[mi][mt][nt][i] = fmaf(scp, dp[mt][i], acc[mi][mt][nt][i]);
             if constexpr (QF == MOE_Q2_ASYM_G32) {
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           }
         }
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) dp[mt] = dc[mt];
+        for (int mt = 0; mt < MTA; ++mt) dp[mt] = dc[mt];
         scp = scc;
         mnp = mnc;
       }
@@ -389,18 +391,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   store_a(0);
   wait_dma();
   __syncthreads();
-  for (int kc = 0; kc < nchunks; ++kc) {
-    const int buf = kc & 1;
-    const bool more = kc + 1 < nchunks;
-    if (more) {
-      dma_b(kc + 1, buf ^ 1);
-      load_a(kc + 1);
+  // the chunk loop, specialised by the number of 16-row M tiles that hold
+  // tokens of the expert (a partial tile skips the products of its empty ones)
+  auto chunks = [&](auto mta_c) {
+    for (int kc = 0; kc < nchunks; ++kc) {
+      const int buf = kc & 1;
+      const bool more = kc + 1 < nchunks;
+      if (more) {
+        dma_b(kc + 1, buf ^ 1);
+        load_a(kc + 1);
+      }
+      compute(buf, mta_c);
+      if (more) store_a(buf ^ 1);
+      wait_dma();
+      __syncthreads();
     }
-    compute(buf);
-    if (more) store_a(buf ^ 1);
-    wait_dma();
-    __syncthreads();
-  }
+  };
+  const int mt_act = min(4, (n_rows - m0 + 15) / 16);  // uniform
+  if (mt_act <= 1) chunks(std::integral_constant<int, 1>{});
+  else if (mt_act == 2) chunks(std::integral_constant<int, 2>{});
+  else if (mt_act == 3) chunks(std::integral_constant<int, 3>{});
+  else chunks(std::integral_constant<int, 4>{});
 
   // ---- epilogue: D lane l holds token rows 4 (l / 16) + i of each M tile, column ln
   constexpr float kUnit = QF == MOE_Q4_SYM_G32 ? 16.f : 4.f;  // the codes' 1/16 or 1/4, exactly
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             const float g = acc[0][mt][nt][i] * kUnit, u = acc[1][mt][nt][i] * kUnit;
             // silu(g) = g / (1 + e^-g), the quotient as a product with the
             // hardware reciprocal (within 2 ulp: far below the bf16 rounding)
-            const float sg = g * __builtin_amdgcn_rcpf(1.0f + expf(-g));
+            const float sg = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896341f));
             hrow[n] = f32_to_bf16(sg * u);
           }
         }
