@@ -13,9 +13,11 @@ Prints one JSON line (rank 0, N = 1):
                algorithmic bytes per launch / HIP-event time per launch
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 plus extra fields: expert-weight GB/s of the whole layer, the same decode steps
-and gate/up launches replayed from captured HIP graphs, prefill tokens/s.
+and gate/up launches replayed from captured HIP graphs, prefill tokens/s, the
+5-token verify batch and one decode step through the 48-layer 2-bit stack at
+batch 1 and 8 (expert planes filled on the device).
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-prefill] [--no-graph]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-prefill] [--no-graph] [--no-stack]
 """
 from __future__ import annotations
 
@@ -63,6 +65,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 4096-token prefill figure")
     ap.add_argument("--prefill-steps", type=int, default=16)
     ap.add_argument("--kernel-reps", type=int, default=2000)
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the verify batch (5 tokens, 2-bit) and the 48-layer 2-bit stack figures")
+    ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra timing of the same steps replayed from captured HIP graphs")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -240,6 +245,9 @@ def main():
         extra["prefill_frac_of_bf16_mfma"] = flops / (pms * 1e-3) / 2.5e15
         log(f"prefill: {pms:.3f} ms/layer, {extra['prefill_tok_s']:.0f} tok/s")
 
+    if not args.no_stack:
+        extra.update(verify_and_stack(args, dev))
+
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -285,6 +293,75 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def verify_and_stack(args, dev):
+    """Extra figures on the 2-bit format, with expert planes filled on the device:
+    the speculative-verify batch (5 tokens through one layer, 16 layer copies
+    rotating) and one decode step through the 48-layer stack at batch 1 and 8."""
+    import torch
+
+    import synth
+    from sparse_moe_router_amd import api, workload
+    from synth import torch_io
+    out = {}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+
+    vs = synth.SPECS["verify"]
+    vlayers = [api.Layer(**torch_io.device_filled_kwargs(vs, c, dev)) for c in range(args.copies)]
+    xv = torch_io.x_tensor(synth.gen_x(vs, seed=0, tokens=64 * vs.tokens).storage, vs.act, dev)
+    ws = api.workspace(vlayers[0], vs.tokens, dev)
+    yv = torch.empty((vs.tokens, vs.hidden), dtype=torch.float32, device=dev)
+
+    def vstep(i):
+        t0 = (i % 64) * vs.tokens
+        api.moe_layer_forward(vlayers[i % args.copies], xv[t0:t0 + vs.tokens], vs.tokens, yv, ws=ws, stream=stream)
+
+    for i in range(50):
+        vstep(i)
+    torch.cuda.synchronize()
+    n = max(200, args.steps // 4)
+    start.record(stream)
+    for i in range(n):
+        vstep(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / n
+    out["verify_T5_q2_us_per_step"] = us
+    out["verify_T5_q2_tok_s"] = vs.tokens / (us * 1e-6)
+    log(f"verify (T=5, 2-bit): {us:.2f} us/step")
+    del vlayers, ws
+    torch.cuda.empty_cache()
+
+    ss = synth.SPECS["stack_t1"]
+    t0 = time.time()
+    stack = [api.Layer(**torch_io.device_filled_kwargs(ss, l, dev)) for l in range(ss.n_layers)]
+    torch.cuda.synchronize()
+    log(f"48-layer 2-bit stack filled on the device in {time.time() - t0:.1f}s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+    for T in (1, 8):
+        spec = synth.SPECS["stack_t1" if T == 1 else "stack_t8"]
+        ws = api.workspace(stack[0], T, dev)
+        base = torch_io.x_tensor(synth.gen_x(spec, seed=0, tokens=T).storage, spec.act, dev)
+        xs = [base.clone() for _ in range(args.stack_steps + 2)]  # each step starts from the same x
+        for k in range(2):
+            api.moe_stack_forward(stack, xs[k], T, ws=ws, stream=stream)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(args.stack_steps):
+            api.moe_stack_forward(stack, xs[2 + k], T, ws=ws, stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) * 1e3 / args.stack_steps
+        out[f"stack48_q2_T{T}_us_per_step"] = us
+        out[f"stack48_q2_T{T}_tok_s"] = T / (us * 1e-6)
+        if T == 1:
+            b = ss.n_layers * workload.spec_layer_bytes(ss, ss.top_k, tokens=1)
+            out["stack48_q2_T1_algorithmic_GBps"] = b / (us * 1e-6) / 1e9
+        log(f"48-layer stack, T={T}: {us:.1f} us/step ({T / (us * 1e-6):.0f} tok/s)")
+        del ws, xs
+    return out
 
 
 def cpu_baseline(spec, ld):

@@ -8,7 +8,7 @@
 // expert's tokens.  A row's 32-element groups are spread over LPR lanes (one
 // group per lane at H = 2048: each lane loads 16 B of 4-bit codes and one fp16
 // scale per row); partial dot products are reduced over those LPR lanes.
-#include "gemv_tile.h"
+#include "gemv_one.h"
 #include "topk.h"
 
 namespace moe {
@@ -148,93 +148,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_s
 // ---- one token, H <= 2048 (one 32-element group per lane) ----------------
 
 constexpr int kFusedRpw1 = 2;  // rows per wave of the one-token gate/up kernels
-
-// The token's activations staged once per block in LDS, prepared for
-// group_acc: group g's 16 words of pairs in q[0..3][g], its offset term in
-// c[g] (lane-contiguous: every read below is conflict-free).
-struct XLds {
-  uint4 q[4][64];
-  float c[64];
-};
-
-// One wave stages x (lane = group; groups past H / 32 repeat the last one).
-template <int QF>
-__device__ __forceinline__ void stage_x1(const void* x, int H, int lane, XLds& xs) {
-  XGroup<QF, MOE_ACT_BF16> xg;
-  xg.load_raw(x, (size_t)min(lane, H / kGroup - 1) * kGroup);
-  xg.prep();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) xs.q[i][lane] = make_uint4(xg.p[4 * i], xg.p[4 * i + 1], xg.p[4 * i + 2], xg.p[4 * i + 3]);
-  xs.c[lane] = xg.c;
-}
-
-template <int QF>
-__device__ __forceinline__ void read_x1(const XLds& xs, int lane, XGroup<QF, MOE_ACT_BF16>& xg) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 v = xs.q[i][lane];
-    xg.p[4 * i] = v.x; xg.p[4 * i + 1] = v.y; xg.p[4 * i + 2] = v.z; xg.p[4 * i + 3] = v.w;
-  }
-  xg.c = xs.c[lane];
-  xg.sx = xg.c;
-}
-
-// The 2 RPW per-lane partial sums of a wave (gate rows 0..RPW-1, then up
-// rows) reduced over the 64 lanes together: a permlane32 swap pairs gate row
-// i with up row i (lanes < 32 keep the gate sum), a permlane16 swap halves
-// the values again, one DPP rotate by 8 when RPW = 4, then DPP steps within
-// the remaining 16 or 8 lanes.  Afterwards lane (32 / RPW) i (i < RPW) holds
-// gate row i in *g and up row i in *u.
-template <int RPW>
-__device__ __forceinline__ void reduce_gu1(const float (&v)[2 * RPW], int lane, float* g, float* u) {
-  static_assert(RPW == 1 || RPW == 2 || RPW == 4, "one, two or four rows per wave");
-  auto f = [](uint32_t b) { return __uint_as_float(b); };
-  auto b = [](float x) { return __float_as_uint(x); };
-  if constexpr (RPW == 1) {
-    const auto r0 = __builtin_amdgcn_permlane32_swap(b(v[0]), b(v[1]), false, false);
-    float sum = f(r0[0]) + f(r0[1]);  // lanes < 32: gate, >= 32: up
-    const auto r1 = __builtin_amdgcn_permlane16_swap(b(sum), b(sum), false, false);
-    sum = f(r1[0]) + f(r1[1]);
-    sum += dpp_f<kDppXor1>(sum);
-    sum += dpp_f<kDppXor2>(sum);
-    sum += dpp_f<kDppHalfMirror>(sum);
-    sum += dpp_f<kDppMirror>(sum);
-    const auto r = __builtin_amdgcn_permlane32_swap(b(sum), b(sum), false, false);
-    *g = f(r[0]);
-    *u = f(r[1]);
-    return;
-  }
-  float w[RPW];
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const auto r = __builtin_amdgcn_permlane32_swap(b(v[i]), b(v[i + RPW]), false, false);
-    w[i] = f(r[0]) + f(r[1]);
-  }
-  float x[RPW / 2 + (RPW == 1)];
-#pragma unroll
-  for (int i = 0; i < RPW / 2; ++i) {
-    const auto r = __builtin_amdgcn_permlane16_swap(b(w[i]), b(w[i + RPW / 2]), false, false);
-    x[i] = f(r[0]) + f(r[1]);
-  }
-  float sum;
-  if constexpr (RPW == 4) {
-    const bool hi = (lane & 8) != 0;
-    const float keep = hi ? x[1] : x[0], give = hi ? x[0] : x[1];
-    sum = keep + dpp_f<kDppRor8>(give);
-    sum += dpp_f<kDppXor1>(sum);
-    sum += dpp_f<kDppXor2>(sum);
-    sum += dpp_f<kDppHalfMirror>(sum);
-  } else {
-    sum = x[0];
-    sum += dpp_f<kDppXor1>(sum);
-    sum += dpp_f<kDppXor2>(sum);
-    sum += dpp_f<kDppHalfMirror>(sum);
-    sum += dpp_f<kDppMirror>(sum);
-  }
-  const auto r = __builtin_amdgcn_permlane32_swap(b(sum), b(sum), false, false);  // gate half | up half
-  *g = f(r[0]);
-  *u = f(r[1]);
-}
 
 // gate/up + SwiGLU of RPW rows (rbase ..) of one expert for one token, with
 // the weight rows already requested and x in LDS; h row hrow.
@@ -428,6 +341,7 @@ hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
   if (mfma_ok(a)) return launch_mfma_gateup(a, s);
   if (gateup1_ok(a))
     return a.qfmt == MOE_Q4_SYM_G32 ? gateup1_q<MOE_Q4_SYM_G32>(a, s) : gateup1_q<MOE_Q2_ASYM_G32>(a, s);
+  if (gateup_sb_ok(a)) return launch_gateup_sb(a, s);
   return a.qfmt == MOE_Q4_SYM_G32 ? dispatch_act<MOE_Q4_SYM_G32>(a, true, s) : dispatch_act<MOE_Q2_ASYM_G32>(a, true, s);
 }
 
@@ -438,6 +352,7 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (mfma_ok(a)) return launch_mfma_down(a, s);
   if (down1_ok(a)) return a.qfmt == MOE_Q4_SYM_G32 ? down1_q<MOE_Q4_SYM_G32>(a, s) : down1_q<MOE_Q2_ASYM_G32>(a, s);
+  if (down_sb_ok(a)) return launch_down_sb(a, s);
   return a.qfmt == MOE_Q4_SYM_G32 ? dispatch_act<MOE_Q4_SYM_G32>(a, false, s) : dispatch_act<MOE_Q2_ASYM_G32>(a, false, s);
 }
 
@@ -746,7 +661,7 @@ bool down1_ok(const FfnArgs& a) {
 }
 
 bool fused_decode_ok(int T, int K, int E, int H, int I, int act) {
-  return act == MOE_ACT_BF16 && T * K <= kFusedMaxPairs && K <= 64 && E <= 64 * kRegLogits && H <= 64 * kGroup &&
+  return act == MOE_ACT_BF16 && T == 1 && T * K <= kFusedMaxPairs && K <= 64 && E <= 64 * kRegLogits && H <= 64 * kGroup &&
          I <= 64 * kGroup;
 }
 

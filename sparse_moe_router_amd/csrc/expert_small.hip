@@ -1,0 +1,191 @@
+// Expert SwiGLU FFNs for small batches (a few tokens per expert: speculative
+// verify, batched decode, the stack at batch 8), with in-register dequant
+// (low-bit weights: page 1 "How Strata Makes the Impossible Possible"; SwiGLU
+// expert sub-networks: page 2 "Layer 1"; shared expert: page 5).
+//
+// Block row y is sorted position y (the pairs sorted by expert, as
+// moe_permute orders them) and works only if y is its expert's first
+// position; then it owns all of the expert's tokens (sorted positions y ..
+// y + n - 1); the last block row is the shared expert (all T tokens).  The
+// expert's weight rows are loaded and unpacked once; the tokens' activations
+// are staged in LDS, prepared, chunk by chunk, and every token reuses the
+// unpacked codes.
+#include "gemv_one.h"
+
+namespace moe {
+
+constexpr int kSbTok = 8;  // tokens staged per chunk
+constexpr int kSbRpw = 2;  // gate/up rows per wave
+constexpr int kSbLpr = 8;  // down: lanes per row
+constexpr int kSbMaxPairs = 256;  // T K of the small-batch path (one block row per sorted position)
+
+// The expert of block row y: first sorted position lo and token count n, or
+// false when y is not the first position of its expert.  Shared row: y == ny.
+__device__ __forceinline__ bool sb_work(const FfnArgs& a, int ny, int y, int* expert, int* lo, int* n) {
+  if (y == ny) {
+    *expert = -1; *lo = 0; *n = a.T;
+    return true;
+  }
+  const int p = a.sorted_pairs[y];
+  const int pp = y > 0 ? a.sorted_pairs[y - 1] : p;
+  const int e = a.ids[p];
+  if (y > 0 && a.ids[pp] == e) return false;
+  *expert = e; *lo = y; *n = a.offsets[e + 1] - y;
+  return true;
+}
+
+// token of the expert's jj-th sorted position
+__device__ __forceinline__ int sb_token(const FfnArgs& a, bool shared, int lo, int jj) {
+  return shared ? jj : a.sorted_pairs[lo + jj] / a.K;
+}
+
+// gate/up + SwiGLU: wave w owns rows (blockIdx.x * 4 + w) * RPW .. + RPW - 1
+// of gate and up, one 32-element group of H per lane (H <= 2048).
+template <int QF>
+__global__ __launch_bounds__(256) void k_gateup_sb(FfnArgs a, int ny) {
+  __shared__ XLds xs[kSbTok];
+  constexpr int RPW = kSbRpw;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int e, lo, n;
+  if (!sb_work(a, ny, blockIdx.y, &e, &lo, &n)) return;
+  const bool shared = e < 0;
+  const int rbase = (blockIdx.x * 4 + wave) * RPW;
+  RowTile<QF, RPW, 1> tg, tu;
+  tg.load(expert_view<QF>(shared ? a.sgate : a.gate, shared ? 0 : e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+  tu.load(expert_view<QF>(shared ? a.sup : a.up, shared ? 0 : e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+  const bool gok = lane < a.H / kGroup;
+  uint32_t bg[RPW][16], bu[RPW][16];
+  bool unpacked = false;
+  void* out = shared ? a.hs : a.h;
+  for (int c0 = 0; c0 < n; c0 += kSbTok) {
+    const int nc = min(kSbTok, n - c0);
+    if (c0 > 0) __syncthreads();  // the previous chunk's readers are done
+    for (int j = wave; j < nc; j += 4) stage_x1<QF>(reinterpret_cast<const uint16_t*>(a.x) +
+                                                        (size_t)sb_token(a, shared, lo, c0 + j) * a.H, a.H, lane, xs[j]);
+    __syncthreads();
+    if (!unpacked) {  // once the weights are here (after the first staging, so that x and w overlap)
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        unpack_group<QF>(tg.c[rr][0], bg[rr]);
+        unpack_group<QF>(tu.c[rr][0], bu[rr]);
+      }
+      unpacked = true;
+    }
+    for (int j = 0; j < nc; ++j) {
+      XGroup<QF, MOE_ACT_BF16> xg;
+      read_x1<QF>(xs[j], lane, xg);
+      float v[2 * RPW];
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const float gv = group_acc_unpacked<QF>(0.f, bg[rr], tg.s[rr][0], tg.m[rr][0], xg);
+        const float uv = group_acc_unpacked<QF>(0.f, bu[rr], tu.s[rr][0], tu.m[rr][0], xg);
+        v[rr] = gok ? gv : 0.f;
+        v[RPW + rr] = gok ? uv : 0.f;
+      }
+      float g, u;
+      reduce_gu1<RPW>(v, lane, &g, &u);
+      constexpr int kStride = 32 / RPW;
+      const int r = rbase + lane / kStride;
+      if (lane < 32 && (lane & (kStride - 1)) == 0 && r < a.I)
+        store_act<MOE_ACT_BF16>(out, (size_t)(lo + c0 + j) * a.I + r, silu(g) * u);
+    }
+  }
+}
+
+// down projection, fp32 out: 8 lanes per row (8 rows per wave, 32 per
+// block), lane sub of a row owning the groups sub + 8 j (j < GPL, I <= 1024).
+// h of each chunk of tokens is staged in LDS, prepared: [token][4][G] uint4
+// pairs and [token][G] offset terms.
+template <int QF, int GPL>
+__global__ __launch_bounds__(256) void k_down_sb(FfnArgs a, int ny) {
+  extern __shared__ __align__(16) uint32_t lds_sb[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int e, lo, n;
+  if (!sb_work(a, ny, blockIdx.y, &e, &lo, &n)) return;
+  const bool shared = e < 0;
+  const int G = a.I / kGroup;
+  uint4* hq = reinterpret_cast<uint4*>(lds_sb);             // [kSbTok][4][G]
+  float* hc = reinterpret_cast<float*>(lds_sb + kSbTok * 16 * G);  // [kSbTok][G]
+  const int rsub = lane >> 3, sub = lane & 7;
+  const int rbase = (blockIdx.x * 4 + wave) * 8;
+  RowTile<QF, 1, GPL> tw;
+  tw.load(expert_view<QF>(shared ? a.sdown : a.down, shared ? 0 : e, a.H, a.I), rbase, rsub, kSbLpr, a.H, sub, kSbLpr);
+  uint32_t b[GPL][16];
+  bool unpacked = false;
+  const void* hin = shared ? a.hs : a.h;
+  float* out = shared ? a.so : a.o;
+  const int r = rbase + rsub;
+  for (int c0 = 0; c0 < n; c0 += kSbTok) {
+    const int nc = min(kSbTok, n - c0);
+    if (c0 > 0) __syncthreads();
+    for (int it = threadIdx.x; it < nc * G; it += 256) {  // (token, group) items
+      const int j = it / G, g = it - j * G;
+      XGroup<QF, MOE_ACT_BF16> hg;
+      hg.load_raw(hin, (size_t)(lo + c0 + j) * a.I + (size_t)g * kGroup);
+      hg.prep();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hq[(j * 4 + i) * G + g] = make_uint4(hg.p[4 * i], hg.p[4 * i + 1], hg.p[4 * i + 2], hg.p[4 * i + 3]);
+      hc[j * G + g] = hg.c;
+    }
+    __syncthreads();
+    if (!unpacked) {
+#pragma unroll
+      for (int gi = 0; gi < GPL; ++gi) unpack_group<QF>(tw.c[0][gi], b[gi]);
+      unpacked = true;
+    }
+    for (int j = 0; j < nc; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < GPL; ++gi) {
+        const int g = min(sub + 8 * gi, G - 1);
+        XGroup<QF, MOE_ACT_BF16> hg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = hq[(j * 4 + i) * G + g];
+          hg.p[4 * i] = v.x; hg.p[4 * i + 1] = v.y; hg.p[4 * i + 2] = v.z; hg.p[4 * i + 3] = v.w;
+        }
+        hg.c = hc[j * G + g];
+        hg.sx = hg.c;
+        const float v = group_acc_unpacked<QF>(acc, b[gi], tw.s[0][gi], tw.m[0][gi], hg);
+        acc = sub + 8 * gi < G ? v : acc;
+      }
+      acc += dpp_f<kDppXor1>(acc);
+      acc += dpp_f<kDppXor2>(acc);
+      acc += dpp_f<kDppHalfMirror>(acc);
+      if (sub == 0 && r < a.H) out[(size_t)(lo + c0 + j) * a.H + r] = acc;
+    }
+  }
+}
+
+bool gateup_sb_ok(const FfnArgs& a) {
+  return a.T > 1 && a.T * a.K <= kSbMaxPairs && a.act == MOE_ACT_BF16 && a.H <= 64 * kGroup;
+}
+bool down_sb_ok(const FfnArgs& a) {
+  return a.T > 1 && a.T * a.K <= kSbMaxPairs && a.act == MOE_ACT_BF16 && a.I <= 32 * kGroup;
+}
+
+hipError_t launch_gateup_sb(const FfnArgs& a, hipStream_t s) {
+  const int ny = a.T * a.K;
+  const dim3 grid((a.I + 4 * kSbRpw - 1) / (4 * kSbRpw), ny + (a.n_shared && a.hs ? 1 : 0));
+  if (a.qfmt == MOE_Q4_SYM_G32) k_gateup_sb<MOE_Q4_SYM_G32><<<grid, 256, 0, s>>>(a, ny);
+  else k_gateup_sb<MOE_Q2_ASYM_G32><<<grid, 256, 0, s>>>(a, ny);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_sb(const FfnArgs& a, hipStream_t s) {
+  const int ny = a.T * a.K;
+  const int G = a.I / kGroup, gpl = (G + 7) / 8;
+  const dim3 grid((a.H + 31) / 32, ny + (a.n_shared && a.so ? 1 : 0));
+  const size_t lds = (size_t)kSbTok * 17 * G * 4;
+  auto go = [&](auto kern) { kern<<<grid, 256, lds, s>>>(a, ny); };
+  if (a.qfmt == MOE_Q4_SYM_G32) {
+    if (gpl <= 1) go(k_down_sb<MOE_Q4_SYM_G32, 1>); else if (gpl == 2) go(k_down_sb<MOE_Q4_SYM_G32, 2>);
+    else if (gpl == 3) go(k_down_sb<MOE_Q4_SYM_G32, 3>); else go(k_down_sb<MOE_Q4_SYM_G32, 4>);
+  } else {
+    if (gpl <= 1) go(k_down_sb<MOE_Q2_ASYM_G32, 1>); else if (gpl == 2) go(k_down_sb<MOE_Q2_ASYM_G32, 2>);
+    else if (gpl == 3) go(k_down_sb<MOE_Q2_ASYM_G32, 3>); else go(k_down_sb<MOE_Q2_ASYM_G32, 4>);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -64,6 +64,13 @@ struct FfnArgs {
 };
 hipError_t launch_gateup(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
+// small batches (1 < T, T K <= 256, bf16; H <= 2048 for gate/up, I <= 1024 for
+// down): one block row per sorted position, the expert's codes unpacked once
+// for all its tokens (launch_gateup / launch_down pick them)
+bool gateup_sb_ok(const FfnArgs& a);
+bool down_sb_ok(const FfnArgs& a);
+hipError_t launch_gateup_sb(const FfnArgs& a, hipStream_t s);
+hipError_t launch_down_sb(const FfnArgs& a, hipStream_t s);
 // matrix-core grouped GEMMs for many tokens per expert (launch_gateup and
 // launch_down take this path themselves when mfma_ok holds)
 bool mfma_ok(const FfnArgs& a);
@@ -84,8 +91,8 @@ struct CombineArgs {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- fused decode path
-// gate/up with the routing (top-K, permutation) recomputed per block: T*K <= 128,
-// K <= 64, E <= 1024, H, I <= 2048, bf16 activations
+// one token: gate/up with the routing (top-K, permutation) recomputed per
+// block: K <= 64, E <= 1024, H, I <= 2048, bf16 activations
 bool fused_decode_ok(int T, int K, int E, int H, int I, int act);
 hipError_t launch_fused_gateup(const RouterArgs& r, const PermuteArgs& pm, const FfnArgs& a, hipStream_t s);
 // one token: down projection fused with the combine (K <= 16, E <= 512, I <= 1024);

@@ -37,3 +37,30 @@ def x_tensor(storage: np.ndarray, act: str, device) -> torch.Tensor:
     if act == ACT_BF16:
         return torch.from_numpy(np.ascontiguousarray(storage).view(np.int16)).to(device).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(storage, dtype=np.float32)).to(device)
+
+
+def device_filled_kwargs(spec, layer: int, device, seed: int = 0) -> dict:
+    """Keyword arguments of one layer whose expert planes are filled on the
+    device, for timing runs over many layers (the stack): uniform random
+    codes, fp16 scales s = 0.0274 U(0.85, 1.15) and, for the 2-bit format,
+    minima m = -1.5 s (the stand-in expert distribution of the stack recipe);
+    the router and its bias come from gen_router as for every other layer."""
+    from . import Q2, gen_router
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1_000_003 + spec.family * 10_007 + layer) & 0x7FFFFFFF)
+    bits = 2 if spec.qfmt == Q2 else 4
+
+    def mat(n, rows, cols):
+        codes = torch.randint(0, 256, (n, rows, cols * bits // 8), dtype=torch.uint8, device=device, generator=g)
+        s = (0.0274 * (0.85 + 0.3 * torch.rand((n, rows, cols // 32), device=device, generator=g))).half()
+        mins = (-1.5 * s.float()).half().view(torch.int16) if bits == 2 else None
+        return codes, s.view(torch.int16), mins
+
+    def experts(n):
+        return dict(gate=mat(n, spec.inter, spec.hidden), up=mat(n, spec.inter, spec.hidden),
+                    down=mat(n, spec.hidden, spec.inter))
+
+    w, b = gen_router(spec, seed=seed, layer=layer)
+    return dict(hidden=spec.hidden, inter=spec.inter, n_experts=spec.n_experts, top_k=spec.top_k, qfmt=spec.qfmt,
+                act=spec.act, router_w=_t(w, device), router_b=_t(b, device), routed=experts(spec.n_experts),
+                shared=experts(1) if spec.n_shared else None)
