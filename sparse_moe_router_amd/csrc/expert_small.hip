@@ -7,9 +7,10 @@
 // moe_permute orders them) and works only if y is its expert's first
 // position; then it owns all of the expert's tokens (sorted positions y ..
 // y + n - 1); the last block row is the shared expert (all T tokens).  The
-// expert's weight rows are loaded and unpacked once; the tokens' activations
-// are staged in LDS, prepared, chunk by chunk, and every token reuses the
-// unpacked codes.
+// expert's weight rows are loaded once; the tokens' activations are staged in
+// LDS, prepared, chunk by chunk.  gate/up keeps its codes packed in registers
+// and unpacks them again for every token (unpacked, they would cost two waves
+// per SIMD of occupancy); down unpacks its codes once for all the tokens.
 #include "gemv_one.h"
 
 namespace moe {
@@ -42,7 +43,7 @@ __device__ __forceinline__ int sb_token(const FfnArgs& a, bool shared, int lo, i
 // gate/up + SwiGLU: wave w owns rows (blockIdx.x * 4 + w) * RPW .. + RPW - 1
 // of gate and up, one 32-element group of H per lane (H <= 2048).
 template <int QF>
-__global__ __launch_bounds__(256) void k_gateup_sb(FfnArgs a, int ny) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gateup_sb(FfnArgs a, int ny) {
   __shared__ XLds xs[kSbTok];
   constexpr int RPW = kSbRpw;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -55,7 +56,6 @@ __global__ __launch_bounds__(256) void k_gateup_sb(FfnArgs a, int ny) {
   tu.load(expert_view<QF>(shared ? a.sup : a.up, shared ? 0 : e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
   const bool gok = lane < a.H / kGroup;
   uint32_t bg[RPW][16], bu[RPW][16];
-  bool unpacked = false;
   void* out = shared ? a.hs : a.h;
   for (int c0 = 0; c0 < n; c0 += kSbTok) {
     const int nc = min(kSbTok, n - c0);
@@ -63,21 +63,16 @@ __global__ __launch_bounds__(256) void k_gateup_sb(FfnArgs a, int ny) {
     for (int j = wave; j < nc; j += 4) stage_x1<QF>(reinterpret_cast<const uint16_t*>(a.x) +
                                                         (size_t)sb_token(a, shared, lo, c0 + j) * a.H, a.H, lane, xs[j]);
     __syncthreads();
-    if (!unpacked) {  // once the weights are here (after the first staging, so that x and w overlap)
-#pragma unroll
-      for (int rr = 0; rr < RPW; ++rr) {
-        unpack_group<QF>(tg.c[rr][0], bg[rr]);
-        unpack_group<QF>(tu.c[rr][0], bu[rr]);
-      }
-      unpacked = true;
-    }
     for (int j = 0; j < nc; ++j) {
       XGroup<QF, MOE_ACT_BF16> xg;
       read_x1<QF>(xs[j], lane, xg);
       float v[2 * RPW];
 #pragma unroll
       for (int rr = 0; rr < RPW; ++rr) {
+        __builtin_amdgcn_sched_barrier(0);
+        unpack_group<QF>(tg.c[rr][0], bg[rr]);
         const float gv = group_acc_unpacked<QF>(0.f, bg[rr], tg.s[rr][0], tg.m[rr][0], xg);
+        unpack_group<QF>(tu.c[rr][0], bu[rr]);
         const float uv = group_acc_unpacked<QF>(0.f, bu[rr], tu.s[rr][0], tu.m[rr][0], xg);
         v[rr] = gok ? gv : 0.f;
         v[RPW + rr] = gok ? uv : 0.f;

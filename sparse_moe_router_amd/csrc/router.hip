@@ -249,6 +249,8 @@ __global__ __launch_bounds__(64) void k_topk_lds(RouterArgs a) {
   }
 }
 
+__device__ __forceinline__ const float* lg_row(const RouterArgs& a, int t) { return a.logits + (size_t)t * a.E; }
+
 // Small batches (T*K <= 256, E <= 1024): top-K of every token and the stable
 // token -> expert permutation in one block.  Pair p = t*K + k gets rank
 // #{q : (e_q, q) < (e_p, p)}; offsets[e] is the first rank with expert >= e.
@@ -257,9 +259,32 @@ __global__ __launch_bounds__(256) void k_route_small(RouterArgs a, PermuteArgs p
   __shared__ int32_t s_ids[kSmallRoutePairs];
   __shared__ int32_t s_sorted[kSmallRoutePairs];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int t = wave; t < a.T; t += 4)
-    wave_topk_regs<PL>(a.logits + (size_t)t * a.E, a.E, a.K, lane, a.ids + (size_t)t * a.K,
-                       a.wts + (size_t)t * a.K, s_ids + t * a.K);
+  if constexpr (PL <= 8) {
+    if (a.K <= 64) {  // consecutive experts per lane: one wave maximum and one ballot per round
+      for (int t = wave; t < a.T; t += 4) {
+        const float* lg = a.logits + (size_t)t * a.E;
+        LaneSorted<PL> ls;
+        ls.load(lg, a.E, lane);
+        uint32_t mine = 0, top = 0;  // lane k keeps the key of round k
+        for (int k = 0; k < a.K; ++k) {
+          const uint32_t m = ls.round(lane, k, s_ids + t * a.K);
+          if (k == 0) top = m;
+          if (lane == k) mine = m;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        write_topk(mine, s_ids[t * a.K + min(lane, a.K - 1)], top, a.K, lane, a.ids + (size_t)t * a.K,
+                   a.wts + (size_t)t * a.K);
+      }
+    } else {
+      for (int t = wave; t < a.T; t += 4)
+        wave_topk_regs<PL>(lg_row(a, t), a.E, a.K, lane, a.ids + (size_t)t * a.K, a.wts + (size_t)t * a.K,
+                           s_ids + t * a.K);
+    }
+  } else {
+    for (int t = wave; t < a.T; t += 4)
+      wave_topk_regs<PL>(lg_row(a, t), a.E, a.K, lane, a.ids + (size_t)t * a.K, a.wts + (size_t)t * a.K,
+                         s_ids + t * a.K);
+  }
   __syncthreads();
   const int n = a.T * a.K, p = threadIdx.x;
   if (p < n) {
