@@ -136,6 +136,8 @@ CASES = [
     (96, 160, 13, 3, 1, "q4_sym_g32", "bf16", True),          # one token: fused down + combine
     (64, 96, 8, 8, 1, "q2_asym_g32", "bf16", False),
     (128, 1024, 20, 16, 1, "q4_sym_g32", "bf16", True),       # K = 16 slots, I = 1024
+    (2048, 768, 64, 10, 25, "q4_sym_g32", "bf16", True),     # small-batch kernels at T K = 250 (<= 256)
+    (2048, 768, 64, 10, 26, "q2_asym_g32", "bf16", True),     # T K = 260: the per-expert GEMV kernels
     (64, 64, 1500, 3, 4, "q4_sym_g32", "bf16", True),         # E > 1024: top-k from LDS
     (96, 64, 1024, 70, 3, "q2_asym_g32", "bf16", True),       # K > 64 slots per token
 ]
@@ -256,6 +258,20 @@ def test_all_tokens_on_one_expert():
     g, _ = full_check(ld, x, strict=False)
     assert np.all(g["ids"] == 11) and np.all(g["w"] == 1.0)
     assert g["offsets"][11] == 0 and g["offsets"][12] == 50
+
+
+@pytest.mark.parametrize("qfmt", ["q4_sym_g32", "q2_asym_g32"])
+def test_hot_expert_many_token_chunks(qfmt):
+    """One expert takes every one of 20 tokens (the small-batch kernels stage
+    its tokens in three chunks of at most 8), at the layer's row shapes."""
+    spec = synth.LayerSpec("hot20", 2048, 24, 2, 768, 20, qfmt, "bf16", 0.0221, 1.1, family=63)
+    ld = synth.gen_layer(spec)
+    ld.router_b = np.zeros(24, np.float32)
+    ld.router_b[3] = 60.0
+    x = synth.gen_x(spec)
+    g, _ = full_check(ld, x, strict=True)
+    assert np.all(g["ids"][:, 0] == 3)
+    assert g["offsets"][4] - g["offsets"][3] == 20
 
 
 def test_zero_tokens_is_noop():
