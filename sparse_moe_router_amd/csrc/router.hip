@@ -252,16 +252,18 @@ __global__ __launch_bounds__(64) void k_topk_lds(RouterArgs a) {
 __device__ __forceinline__ const float* lg_row(const RouterArgs& a, int t) { return a.logits + (size_t)t * a.E; }
 
 // Small batches (T*K <= 256, E <= 1024): top-K of every token and the stable
-// token -> expert permutation in one block.  Pair p = t*K + k gets rank
+// token -> expert permutation in one block of NWV waves (one token per wave
+// up to NWV tokens; 16 waves up to E = 512, 4 above, whose selection state
+// needs more registers).  Pair p = t*K + k gets rank
 // #{q : (e_q, q) < (e_p, p)}; offsets[e] is the first rank with expert >= e.
-template <int PL>
-__global__ __launch_bounds__(256) void k_route_small(RouterArgs a, PermuteArgs pm) {
+template <int PL, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_route_small(RouterArgs a, PermuteArgs pm) {
   __shared__ int32_t s_ids[kSmallRoutePairs];
   __shared__ int32_t s_sorted[kSmallRoutePairs];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if constexpr (PL <= 8) {
     if (a.K <= 64) {  // consecutive experts per lane: one wave maximum and one ballot per round
-      for (int t = wave; t < a.T; t += 4) {
+      for (int t = wave; t < a.T; t += NWV) {
         const float* lg = a.logits + (size_t)t * a.E;
         LaneSorted<PL> ls;
         ls.load(lg, a.E, lane);
@@ -276,12 +278,12 @@ __global__ __launch_bounds__(256) void k_route_small(RouterArgs a, PermuteArgs p
                    a.wts + (size_t)t * a.K);
       }
     } else {
-      for (int t = wave; t < a.T; t += 4)
+      for (int t = wave; t < a.T; t += NWV)
         wave_topk_regs<PL>(lg_row(a, t), a.E, a.K, lane, a.ids + (size_t)t * a.K, a.wts + (size_t)t * a.K,
                            s_ids + t * a.K);
     }
   } else {
-    for (int t = wave; t < a.T; t += 4)
+    for (int t = wave; t < a.T; t += NWV)
       wave_topk_regs<PL>(lg_row(a, t), a.E, a.K, lane, a.ids + (size_t)t * a.K, a.wts + (size_t)t * a.K,
                          s_ids + t * a.K);
   }
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(256) void k_route_small(RouterArgs a, PermuteArgs p
     s_sorted[rank] = e;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e <= a.E; e += 256) {
+  for (int e = threadIdx.x; e <= a.E; e += 64 * NWV) {
     int lo = 0, hi = n;  // first rank with expert >= e
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -362,11 +364,11 @@ bool route_small_ok(int T, int K, int E) { return (int64_t)T * K <= kSmallRouteP
 
 hipError_t launch_route_small(const RouterArgs& a, const PermuteArgs& p, hipStream_t s) {
   switch (regs_per_lane(a.E)) {
-    case 1: k_route_small<1><<<1, 256, 0, s>>>(a, p); break;
-    case 2: k_route_small<2><<<1, 256, 0, s>>>(a, p); break;
-    case 4: k_route_small<4><<<1, 256, 0, s>>>(a, p); break;
-    case 8: k_route_small<8><<<1, 256, 0, s>>>(a, p); break;
-    default: k_route_small<16><<<1, 256, 0, s>>>(a, p); break;
+    case 1: k_route_small<1, 16><<<1, 64 * 16, 0, s>>>(a, p); break;
+    case 2: k_route_small<2, 16><<<1, 64 * 16, 0, s>>>(a, p); break;
+    case 4: k_route_small<4, 16><<<1, 64 * 16, 0, s>>>(a, p); break;
+    case 8: k_route_small<8, 16><<<1, 64 * 16, 0, s>>>(a, p); break;
+    default: k_route_small<16, 4><<<1, 64 * 4, 0, s>>>(a, p); break;
   }
   return hipGetLastError();
 }
