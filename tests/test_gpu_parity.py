@@ -424,6 +424,37 @@ def test_decode_graph_replay(family1):
         assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("T", [5, 8])
+def test_small_batch_graph_replay(T):
+    """Small-batch steps (routing of T tokens in one block, the small-batch expert kernels, the combine)
+    captured in a HIP graph and replayed four times, with eager work of the same layer and a fill kernel
+    between the replays: every replay gives the eager result bit for bit."""
+    spec = synth.LayerSpec("sbgraph", 2048, 64, 10, 768, 4 * T, "q2_asym_g32", "bf16", 0.0221, 1.1, family=73)
+    ld = synth.gen_layer(spec)
+    L = gu.device_layer(ld)
+    xd = gu.x_dev(synth.gen_x(spec), spec.act)
+    ws = api.workspace(L, T, gu.DEV)
+    y_eager = torch.zeros((3 * T, spec.hidden), dtype=torch.float32, device=gu.DEV)
+    for i in range(3):
+        api.moe_layer_forward(L, xd[i * T:(i + 1) * T], T, y_eager[i * T:(i + 1) * T], ws=ws)
+    torch.cuda.synchronize()
+    want = y_eager.cpu().numpy()
+    y = torch.zeros_like(y_eager)
+    scratch = torch.empty((T, spec.hidden), dtype=torch.float32, device=gu.DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for i in range(3):
+            api.moe_layer_forward(L, xd[i * T:(i + 1) * T], T, y[i * T:(i + 1) * T], ws=ws)
+    for rep in range(4):
+        y.zero_()
+        g.replay()
+        api.moe_layer_forward(L, xd[3 * T:4 * T], T, scratch, ws=ws)  # eager step between the replays
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        gu.say(f"T={T} graph replay {rep}: max|dy| = {np.abs(got - want).max():.1e}")
+        assert np.array_equal(got, want)
+
+
 def test_prefill_sampled(family1):
     ld, L = family1
     spec = synth.SPECS["prefill"]
