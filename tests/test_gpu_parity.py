@@ -424,11 +424,12 @@ def test_decode_graph_replay(family1):
         assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("T", [5, 8])
-def test_small_batch_graph_replay(T):
-    """Small-batch steps (routing of T tokens in one block, the small-batch expert kernels, the combine)
-    captured in a HIP graph and replayed four times, with eager work of the same layer and a fill kernel
-    between the replays: every replay gives the eager result bit for bit."""
+@pytest.mark.parametrize("T", [5, 8, 64])
+def test_batch_graph_replay(T):
+    """Steps of T tokens captured in a HIP graph and replayed four times, with eager work of the same layer
+    and a fill kernel between the replays: every replay gives the eager result bit for bit.  T = 5, 8: the
+    routing of all tokens in one block and the small-batch expert kernels; T = 64 (640 pairs on 64 experts):
+    the multi-block top-k and permutation and the matrix-core grouped GEMMs."""
     spec = synth.LayerSpec("sbgraph", 2048, 64, 10, 768, 4 * T, "q2_asym_g32", "bf16", 0.0221, 1.1, family=73)
     ld = synth.gen_layer(spec)
     L = gu.device_layer(ld)
