@@ -121,16 +121,24 @@ __global__ __launch_bounds__(1024) void k_perm_scan(PermuteArgs a, int n_chunks)
   const int E = a.E, tid = threadIdx.x;
   const int per = (E + 1023) / 1024;
   const int e0 = tid * per;
+  // the chunk counts go through in batches of kBatch, all loaded before any is
+  // stored, so that the loads of a batch are in flight together
+  constexpr int kBatch = 8;
   int sum = 0;
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
     int run = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      const size_t q = (size_t)c * E + e;
-      const int v = a.chunk_base[q];
-      a.chunk_base[q] = run;
-      run += v;
+    for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) v[j] = c0 + j < n_chunks ? a.chunk_base[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (c0 + j < n_chunks) {
+          a.chunk_base[(size_t)(c0 + j) * E + e] = run;
+          run += v[j];
+        }
     }
     a.offsets[e] = run;  // count for now, rewritten below by this same thread
     sum += run;
@@ -149,7 +157,14 @@ __global__ __launch_bounds__(1024) void k_perm_scan(PermuteArgs a, int n_chunks)
     if (e >= E) break;
     const int cnt = a.offsets[e];
     a.offsets[e] = off;
-    for (int c = 0; c < n_chunks; ++c) a.chunk_base[(size_t)c * E + e] += off;
+    for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) v[j] = c0 + j < n_chunks ? a.chunk_base[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (c0 + j < n_chunks) a.chunk_base[(size_t)(c0 + j) * E + e] = v[j] + off;
+    }
     off += cnt;
   }
   if (tid == 1023) a.offsets[E] = part[1023];
