@@ -34,24 +34,37 @@ __device__ __forceinline__ int id_bits(int E) {
 }
 
 // One wave scatters pairs [p0, p1) in order; running[e] holds the next free
-// sorted position of expert e (LDS, owned by this wave).
+// sorted position of expert e (LDS, owned by this wave).  The ids of 16
+// rounds of 64 pairs are requested together, before the first round.
 __device__ void scatter_chunk(const PermuteArgs& a, int* running, int p0, int p1, int lane, int nbits) {
-  for (int base = p0; base < p1; base += 64) {
-    const int p = base + lane;
-    const bool valid = p < p1;
-    const int e = valid ? a.ids[p] : 0;
-    const uint64_t same = match_same(e, valid, nbits);
-    const int rank = __popcll(same & lanemask_lt(lane));
-    const int cnt = __popcll(same);
-    int pos = 0;
-    if (valid) pos = running[e] + rank;
-    __syncthreads();
-    if (valid) {
-      a.sorted_pairs[pos] = p;
-      a.pair_pos[p] = pos;
-      if (rank == 0) running[e] += cnt;
+  constexpr int kRounds = 16;
+  for (int b0 = p0; b0 < p1; b0 += 64 * kRounds) {
+    int ev[kRounds];
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int p = b0 + 64 * i + lane;
+      ev[i] = p < p1 ? a.ids[p] : 0;
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int base = b0 + 64 * i;
+      if (base >= p1) break;  // uniform
+      const int p = base + lane;
+      const bool valid = p < p1;
+      const int e = ev[i];
+      const uint64_t same = match_same(e, valid, nbits);
+      const int rank = __popcll(same & lanemask_lt(lane));
+      const int cnt = __popcll(same);
+      int pos = 0;
+      if (valid) pos = running[e] + rank;
+      __syncthreads();
+      if (valid) {
+        a.sorted_pairs[pos] = p;
+        a.pair_pos[p] = pos;
+        if (rank == 0) running[e] += cnt;
+      }
+      __syncthreads();
+    }
   }
 }
 
