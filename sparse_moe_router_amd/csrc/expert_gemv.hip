@@ -587,11 +587,14 @@ __global__ __launch_bounds__(64 * kDown1MaxWaves) void k_fused_down1(FfnArgs a, 
   const int rbase = blockIdx.x * 8;
   const bool has_shared = a.so != nullptr;
   const int nslots = K + (has_shared ? 1 : 0);
-  // the combine's inputs are requested now, not after the products
-  float resid = 0.f;
-  if (threadIdx.x < K) s_w[threadIdx.x] = c.w[threadIdx.x];
-  if (c.x_next && threadIdx.x < 8 && rbase + (int)threadIdx.x < a.H)
-    resid = load_act<MOE_ACT_BF16>(c.x_resid, rbase + threadIdx.x);
+  // the combine's inputs are requested now and used after the products; the
+  // loads are branch-free (clamped indices) and their values stay untouched
+  // until the weights are requested, so no wave waits for them first
+  const float wv = c.w[min((int)threadIdx.x, K - 1)];
+  // bf16 bits of the residual of row rbase + threadIdx.x % 8 (without a
+  // residual, a word of the weights stands in, unused)
+  const uint16_t* rp = c.x_next ? reinterpret_cast<const uint16_t*>(c.x_resid) : reinterpret_cast<const uint16_t*>(c.w);
+  const uint32_t rraw = rp[c.x_next ? min(rbase + (int)(threadIdx.x & 7), a.H - 1) : 0];
   int hrow[SPW], e[SPW];
   bool sh[SPW];
 #pragma unroll
@@ -603,6 +606,7 @@ __global__ __launch_bounds__(64 * kDown1MaxWaves) void k_fused_down1(FfnArgs a, 
   }
   Down1Wave<QF, SPW, GPL> dw;
   dw.load(a, hrow, sh, e, rbase, lane, lds_d1 + wave * down1_wave_words(SPW, a.I / kGroup));
+  if (threadIdx.x < K) s_w[threadIdx.x] = wv;
 #pragma unroll
   for (int js = 0; js < SPW; ++js) {
     const int slot = wave + NW * js;
@@ -616,7 +620,7 @@ __global__ __launch_bounds__(64 * kDown1MaxWaves) void k_fused_down1(FfnArgs a, 
     for (int k = 0; k < K; ++k) acc = fmaf(s_w[k], s_o[k][i], acc);
     if (r < a.H) {
       c.y[r] = acc;
-      if (c.x_next) store_act<MOE_ACT_BF16>(c.x_next, r, resid + acc);
+      if (c.x_next) store_act<MOE_ACT_BF16>(c.x_next, r, bf16_to_f32(rraw) + acc);
     }
   }
 }
