@@ -140,6 +140,8 @@ CASES = [
     (2048, 768, 64, 10, 26, "q2_asym_g32", "bf16", True),     # T K = 260: the per-expert GEMV kernels
     (64, 64, 1500, 3, 4, "q4_sym_g32", "bf16", True),         # E > 1024: top-k from LDS
     (96, 64, 1024, 70, 3, "q2_asym_g32", "bf16", True),       # K > 64 slots per token
+    (64, 64, 8192, 64, 3, "q4_sym_g32", "bf16", True),        # the most experts the ABI takes, K = 64
+    (64, 64, 8192, 64, 1, "q4_sym_g32", "bf16", True),        # the same, one token
 ]
 
 
