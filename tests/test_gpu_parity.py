@@ -458,6 +458,44 @@ def test_batch_graph_replay(T):
         assert np.array_equal(got, want)
 
 
+def test_concurrent_streams_match_sequential(family1):
+    """Calls on distinct streams with distinct outputs and workspaces may run at the same time (the ABI keeps
+    no state): decode steps of the 512-expert layer on one stream and 64-token steps of a 64-expert 2-bit
+    layer on another, enqueued interleaved, give the bits of the same calls run one after another."""
+    ld, L = family1
+    spec = synth.SPECS["decode"]
+    xa = gu.x_dev(synth.gen_x(spec, tokens=8), spec.act)
+    bspec = synth.LayerSpec("streams", 2048, 64, 10, 768, 3 * 64, "q2_asym_g32", "bf16", 0.0221, 1.1, family=74)
+    Lb = gu.device_layer(synth.gen_layer(bspec))
+    xb = gu.x_dev(synth.gen_x(bspec), bspec.act)
+    ws_a, ws_b = api.workspace(L, 1, gu.DEV), api.workspace(Lb, 64, gu.DEV)
+
+    def run(ya, yb, sa, sb):
+        for i in range(8):
+            api.moe_layer_forward(L, xa[i:i + 1], 1, ya[i:i + 1], ws=ws_a, stream=sa)
+            if i < 3:
+                api.moe_layer_forward(Lb, xb[64 * i:64 * (i + 1)], 64, yb[64 * i:64 * (i + 1)], ws=ws_b, stream=sb)
+
+    def outputs():
+        return (torch.zeros((8, spec.hidden), dtype=torch.float32, device=gu.DEV),
+                torch.zeros((3 * 64, bspec.hidden), dtype=torch.float32, device=gu.DEV))
+
+    ya0, yb0 = outputs()
+    cur = torch.cuda.current_stream()
+    run(ya0, yb0, cur, cur)
+    torch.cuda.synchronize()
+    want_a, want_b = ya0.cpu().numpy(), yb0.cpu().numpy()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    for rep in range(3):
+        ya, yb = outputs()
+        torch.cuda.synchronize()  # the fills are done before either stream starts
+        run(ya, yb, sa, sb)
+        torch.cuda.synchronize()
+        da, db = np.abs(ya.cpu().numpy() - want_a).max(), np.abs(yb.cpu().numpy() - want_b).max()
+        gu.say(f"two streams, rep {rep}: max|dy| decode {da:.1e}, batch {db:.1e}")
+        assert np.array_equal(ya.cpu().numpy(), want_a) and np.array_equal(yb.cpu().numpy(), want_b)
+
+
 def test_prefill_sampled(family1):
     ld, L = family1
     spec = synth.SPECS["prefill"]
