@@ -122,15 +122,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // staging: thread -> token row r = tid / 4, 32-k slice q = tid % 4 of the chunk (4 x 16 bytes)
   const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
   const uint16_t* xrow = reinterpret_cast<const uint16_t*>(a.x) + (size_t)min(m0 + r, a.T - 1) * a.H;
-  uint4 st[4];
+  ru32x4_t st[4];  // native vectors: with HIP's uint4 the compiler kept this array in scratch memory
   auto load_x = [&](int kc) {
     const int k = min(kc * kRKC + q * 32, a.H - 32);  // past H: any in-range slice, never used
-    const uint4* src = reinterpret_cast<const uint4*>(xrow + k);
+    const ru32x4_t* src = reinterpret_cast<const ru32x4_t*>(xrow + k);
 #pragma unroll
     for (int i = 0; i < 4; ++i) st[i] = src[i];
   };
   auto store_x = [&](int buf) {
-    uint4* dst = reinterpret_cast<uint4*>(&s_x[buf][r * kRRow + q * 32]);
+    ru32x4_t* dst = reinterpret_cast<ru32x4_t*>(&s_x[buf][r * kRRow + q * 32]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = st[i];
   };
@@ -160,10 +160,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int kc = 0; kc < nchunks; ++kc) {
     const int buf = kc & 1;
     const int steps = min(kRKC, a.H - kc * kRKC) / 32;  // H is a multiple of 32
-    if (kc + 1 < nchunks) {
-      load_x(kc + 1);
-      load_w(kc + 1, wn);
-    }
+    // the next chunk's loads and LDS store are branch-free (indices clamped;
+    // after the last chunk they fill a buffer that is never read), so the
+    // staged values stay in registers and no wait lands before the products
+    load_x(kc + 1);
+    load_w(kc + 1, wn);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j < steps) {
@@ -182,13 +183,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
       }
     }
-    if (kc + 1 < nchunks) {
-      store_x(buf ^ 1);
+    store_x(buf ^ 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wv[j][0] = wn[j][0];
-        wv[j][1] = wn[j][1];
-      }
+    for (int j = 0; j < 4; ++j) {
+      wv[j][0] = wn[j][0];
+      wv[j][1] = wn[j][1];
     }
     __syncthreads();
   }
