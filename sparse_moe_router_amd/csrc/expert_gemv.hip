@@ -178,7 +178,8 @@ __device__ __forceinline__ void gateup_rows1(const FfnArgs& a, bool shared, int 
 // Standalone gate/up for one token (moe_expert_gate_up_q, T = 1): block row
 // k < K computes pair k, whose expert is ids[k], into h row pair_pos[k] (the
 // rank of (ids[k], k)), both from one load of the K ids; row K is the shared
-// expert.  Wave 0 stages x in LDS while the weights are in flight.
+// expert.  Wave 0 requests x before the ids and the weights, and stages it
+// in LDS while the weights are in flight.
 template <int QF, int RPW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MOE_ACT_BF16, 1, 1)))) void
 k_gateup1(FfnArgs a) {
@@ -186,6 +187,10 @@ k_gateup1(FfnArgs a) {
   const int K = a.K, y = blockIdx.y;
   const bool shared = y == K;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // (loads complete in order: requested after the weights, x could only be
+  // staged once they had landed)
+  XGroup<QF, MOE_ACT_BF16> xg;
+  if (wave == 0) load_x1<QF>(a.x, a.H, lane, xg);
   int e = 0, hrow = 0;
   if (!shared) {
     const int id = a.ids[min(lane, K - 1)];
@@ -196,7 +201,7 @@ k_gateup1(FfnArgs a) {
   RowTile<QF, RPW, 1> tg, tu;
   tg.load(expert_view<QF>(shared ? a.sgate : a.gate, e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
   tu.load(expert_view<QF>(shared ? a.sup : a.up, e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
-  if (wave == 0) stage_x1<QF>(a.x, a.H, lane, xs);
+  if (wave == 0) put_x1<QF>(xg, lane, xs);
   __syncthreads();
   gateup_rows1<QF, RPW>(a, shared, hrow, rbase, lane, tg, tu, xs);
 }
@@ -524,6 +529,9 @@ struct Down1Wave {
       for (int k = 1; k < SPW; ++k) { row = js == k ? hrow[k] : row; s0 = js == k ? sh[k] : s0; }
       xg[r].load_raw(s0 ? a.hs : a.h, (size_t)row * a.I + (size_t)g * kGroup);
     }
+    // keep the h loads ahead of the weight loads: loads complete in order, so
+    // h can then be staged while the weight rows are still in flight
+    __builtin_amdgcn_sched_barrier(0);
     const int rsub = lane >> 3, sub = lane & 7;
 #pragma unroll
     for (int js = 0; js < SPW; ++js)

@@ -17,15 +17,27 @@ struct XLds {
   float c[64];
 };
 
-// One wave stages x (lane = group; groups past H / 32 repeat the last one).
+// One wave's share of x: lane = group; groups past H / 32 repeat the last one.
 template <int QF>
-__device__ __forceinline__ void stage_x1(const void* x, int H, int lane, XLds& xs) {
-  XGroup<QF, MOE_ACT_BF16> xg;
+__device__ __forceinline__ void load_x1(const void* x, int H, int lane, XGroup<QF, MOE_ACT_BF16>& xg) {
   xg.load_raw(x, (size_t)min(lane, H / kGroup - 1) * kGroup);
+}
+
+// The loaded group prepared and stored in LDS.
+template <int QF>
+__device__ __forceinline__ void put_x1(XGroup<QF, MOE_ACT_BF16>& xg, int lane, XLds& xs) {
   xg.prep();
 #pragma unroll
   for (int i = 0; i < 4; ++i) xs.q[i][lane] = make_uint4(xg.p[4 * i], xg.p[4 * i + 1], xg.p[4 * i + 2], xg.p[4 * i + 3]);
   xs.c[lane] = xg.c;
+}
+
+// One wave stages x.
+template <int QF>
+__device__ __forceinline__ void stage_x1(const void* x, int H, int lane, XLds& xs) {
+  XGroup<QF, MOE_ACT_BF16> xg;
+  load_x1<QF>(x, H, lane, xg);
+  put_x1<QF>(xg, lane, xs);
 }
 
 template <int QF>
