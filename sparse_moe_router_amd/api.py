@@ -214,14 +214,16 @@ def moe_expert_ffn_q(layer: Layer, x, T, topk_ids, expert_offsets, sorted_pairs,
                                                       w, wn, _stream(stream)))
 
 
+def _gate_up_args(layer, x, T, topk_ids, expert_offsets, sorted_pairs, h, shared_h, stream):
+    return (layer.ref, _x(layer, x, T), int(T), _ptr(topk_ids, torch.int32), _ptr(expert_offsets, torch.int32),
+            _ptr(sorted_pairs, torch.int32), _ptr(h, layer.act_dtype), _ptr(shared_h, layer.act_dtype),
+            _stream(stream))
+
+
 def moe_expert_gate_up_q(layer: Layer, x, T, topk_ids, expert_offsets, sorted_pairs, h, shared_h=None,
                          stream=None):
-    _check("moe_expert_gate_up_q", lib().moe_expert_gate_up_q(layer.ref, _x(layer, x, T), int(T),
-                                                              _ptr(topk_ids, torch.int32),
-                                                              _ptr(expert_offsets, torch.int32),
-                                                              _ptr(sorted_pairs, torch.int32),
-                                                              _ptr(h, layer.act_dtype),
-                                                              _ptr(shared_h, layer.act_dtype), _stream(stream)))
+    _check("moe_expert_gate_up_q", lib().moe_expert_gate_up_q(
+        *_gate_up_args(layer, x, T, topk_ids, expert_offsets, sorted_pairs, h, shared_h, stream)))
 
 
 def moe_expert_down_q(layer: Layer, h, shared_h, T, topk_ids, expert_offsets, sorted_pairs, expert_out,
@@ -244,11 +246,48 @@ def moe_combine(layer: Layer, expert_out, shared_out, pair_pos, topk_w, T, y, x_
                                             _stream(stream)))
 
 
-def moe_layer_forward(layer: Layer, x, T, y, x_next=None, topk_ids=None, topk_w=None, ws=None, stream=None):
+def _layer_forward_args(layer, x, T, y, x_next, topk_ids, topk_w, ws, stream):
     w, wn = _ws(ws)
-    _check("moe_layer_forward", lib().moe_layer_forward(layer.ref, _x(layer, x, T), int(T), _ptr(y, torch.float32),
-                                                        _ptr(x_next, layer.act_dtype), _ptr(topk_ids, torch.int32),
-                                                        _ptr(topk_w, torch.float32), w, wn, _stream(stream)))
+    return (layer.ref, _x(layer, x, T), int(T), _ptr(y, torch.float32), _ptr(x_next, layer.act_dtype),
+            _ptr(topk_ids, torch.int32), _ptr(topk_w, torch.float32), w, wn, _stream(stream))
+
+
+def moe_layer_forward(layer: Layer, x, T, y, x_next=None, topk_ids=None, topk_w=None, ws=None, stream=None):
+    _check("moe_layer_forward", lib().moe_layer_forward(
+        *_layer_forward_args(layer, x, T, y, x_next, topk_ids, topk_w, ws, stream)))
+
+
+class Bound:
+    """One entry point with its arguments checked and marshalled once.
+
+    Calling it enqueues the same call again (same buffers, same stream) through
+    the C ABI with no per-call Python checks, for loops where the host would
+    otherwise take as long as the kernels.  It keeps the tensors it was given
+    alive.  A non-OK status still raises MoeError."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self.name, self.args, self._keep = name, args, keep
+        self.fn = getattr(lib(), name)
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != MOE_OK:
+            _check(self.name, st)
+
+
+def bind_layer_forward(layer: Layer, x, T, y, x_next=None, topk_ids=None, topk_w=None, ws=None,
+                       stream=None) -> Bound:
+    """moe_layer_forward(...) as a Bound call."""
+    return Bound("moe_layer_forward", _layer_forward_args(layer, x, T, y, x_next, topk_ids, topk_w, ws, stream),
+                 (layer, x, y, x_next, topk_ids, topk_w, ws, stream))
+
+
+def bind_expert_gate_up_q(layer: Layer, x, T, topk_ids, expert_offsets, sorted_pairs, h, shared_h=None,
+                          stream=None) -> Bound:
+    """moe_expert_gate_up_q(...) as a Bound call."""
+    return Bound("moe_expert_gate_up_q",
+                 _gate_up_args(layer, x, T, topk_ids, expert_offsets, sorted_pairs, h, shared_h, stream),
+                 (layer, x, topk_ids, expert_offsets, sorted_pairs, h, shared_h, stream))
 
 
 def moe_stack_forward(layers, x_inout, T, y_last=None, ws=None, stream=None):

@@ -137,3 +137,18 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(api, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no non-HIP fallback"):
         api.lib()
+
+
+def test_bound_call_reports_the_status():
+    """api.Bound re-issues one marshalled call: a rejected descriptor raises MoeError with the library's status
+    (nothing is launched), and a T = 0 call is a no-op."""
+    bad = layer(top_k=0)
+    call = api.Bound("moe_layer_forward", (ctypes.byref(bad), FAKE, 4, FAKE, None, None, None, FAKE, 1 << 40, None),
+                     keep=(bad,))
+    for _ in range(2):
+        with pytest.raises(api.MoeError) as e:
+            call()
+        assert e.value.status == api.MOE_E_ARG
+    good = layer()
+    api.Bound("moe_layer_forward", (ctypes.byref(good), None, 0, None, None, None, None, None, 0, None),
+              keep=(good,))()
