@@ -46,23 +46,43 @@ template <int QF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gateup_sb(FfnArgs a, int ny) {
   __shared__ XLds xs[kSbTok];
   constexpr int RPW = kSbRpw;
+  static_assert(kSbTok == 8, "the first chunk is two tokens per wave");
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int y = blockIdx.y;
+  // tokens of the first chunk's positions y + wave and y + wave + 4, read
+  // with the expert lookup (clamped in range; used only below the count)
+  int tok0[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) tok0[k] = y == ny ? wave + 4 * k : a.sorted_pairs[min(y + wave + 4 * k, ny - 1)] / a.K;
   int e, lo, n;
-  if (!sb_work(a, ny, blockIdx.y, &e, &lo, &n)) return;
+  if (!sb_work(a, ny, y, &e, &lo, &n)) return;
   const bool shared = e < 0;
   const int rbase = (blockIdx.x * 4 + wave) * RPW;
+  // the first chunk's activations go out before the weight rows: loads
+  // complete in order, so they are staged while the weights are in flight
+  const int nc0 = min(kSbTok, n);
+  XGroup<QF, MOE_ACT_BF16> x0[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (wave + 4 * k < nc0) load_x1<QF>(reinterpret_cast<const uint16_t*>(a.x) + (size_t)tok0[k] * a.H, a.H, lane, x0[k]);
   RowTile<QF, RPW, 1> tg, tu;
   tg.load(expert_view<QF>(shared ? a.sgate : a.gate, shared ? 0 : e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
   tu.load(expert_view<QF>(shared ? a.sup : a.up, shared ? 0 : e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (wave + 4 * k < nc0) put_x1<QF>(x0[k], lane, xs[wave + 4 * k]);
+  __syncthreads();
   const bool gok = lane < a.H / kGroup;
   uint32_t bg[RPW][16], bu[RPW][16];
   void* out = shared ? a.hs : a.h;
   for (int c0 = 0; c0 < n; c0 += kSbTok) {
     const int nc = min(kSbTok, n - c0);
-    if (c0 > 0) __syncthreads();  // the previous chunk's readers are done
-    for (int j = wave; j < nc; j += 4) stage_x1<QF>(reinterpret_cast<const uint16_t*>(a.x) +
-                                                        (size_t)sb_token(a, shared, lo, c0 + j) * a.H, a.H, lane, xs[j]);
-    __syncthreads();
+    if (c0 > 0) {
+      __syncthreads();  // the previous chunk's readers are done
+      for (int j = wave; j < nc; j += 4) stage_x1<QF>(reinterpret_cast<const uint16_t*>(a.x) +
+                                                          (size_t)sb_token(a, shared, lo, c0 + j) * a.H, a.H, lane, xs[j]);
+      __syncthreads();
+    }
     for (int j = 0; j < nc; ++j) {
       XGroup<QF, MOE_ACT_BF16> xg;
       read_x1<QF>(xs[j], lane, xg);
@@ -103,26 +123,40 @@ __global__ __launch_bounds__(256) void k_down_sb(FfnArgs a, int ny) {
   float* hc = reinterpret_cast<float*>(lds_sb + kSbTok * 16 * G);  // [kSbTok][G]
   const int rsub = lane >> 3, sub = lane & 7;
   const int rbase = (blockIdx.x * 4 + wave) * 8;
-  RowTile<QF, 1, GPL> tw;
-  tw.load(expert_view<QF>(shared ? a.sdown : a.down, shared ? 0 : e, a.H, a.I), rbase, rsub, kSbLpr, a.H, sub, kSbLpr);
-  uint32_t b[GPL][16];
-  bool unpacked = false;
   const void* hin = shared ? a.hs : a.h;
   float* out = shared ? a.so : a.o;
+  // one (token, group) item of h per thread and chunk (G <= 32, so a chunk
+  // has at most 256 items); the first chunk's h goes out before the weight
+  // rows, so it is staged while they are in flight
+  auto put_h = [&](int it, XGroup<QF, MOE_ACT_BF16>& hg) {
+    const int j = it / G, g = it - j * G;
+    hg.prep();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hq[(j * 4 + i) * G + g] = make_uint4(hg.p[4 * i], hg.p[4 * i + 1], hg.p[4 * i + 2], hg.p[4 * i + 3]);
+    hc[j * G + g] = hg.c;
+  };
+  const int it = threadIdx.x;
+  XGroup<QF, MOE_ACT_BF16> h0;
+  const bool item0 = it < min(kSbTok, n) * G;
+  if (item0) h0.load_raw(hin, (size_t)(lo + it / G) * a.I + (size_t)(it % G) * kGroup);
+  RowTile<QF, 1, GPL> tw;
+  tw.load(expert_view<QF>(shared ? a.sdown : a.down, shared ? 0 : e, a.H, a.I), rbase, rsub, kSbLpr, a.H, sub, kSbLpr);
+  if (item0) put_h(it, h0);
+  __syncthreads();
+  uint32_t b[GPL][16];
+  bool unpacked = false;
   const int r = rbase + rsub;
   for (int c0 = 0; c0 < n; c0 += kSbTok) {
     const int nc = min(kSbTok, n - c0);
-    if (c0 > 0) __syncthreads();
-    for (int it = threadIdx.x; it < nc * G; it += 256) {  // (token, group) items
-      const int j = it / G, g = it - j * G;
-      XGroup<QF, MOE_ACT_BF16> hg;
-      hg.load_raw(hin, (size_t)(lo + c0 + j) * a.I + (size_t)g * kGroup);
-      hg.prep();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hq[(j * 4 + i) * G + g] = make_uint4(hg.p[4 * i], hg.p[4 * i + 1], hg.p[4 * i + 2], hg.p[4 * i + 3]);
-      hc[j * G + g] = hg.c;
+    if (c0 > 0) {
+      __syncthreads();  // the previous chunk's readers are done
+      if (it < nc * G) {
+        XGroup<QF, MOE_ACT_BF16> hg;
+        hg.load_raw(hin, (size_t)(lo + c0 + it / G) * a.I + (size_t)(it % G) * kGroup);
+        put_h(it, hg);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     if (!unpacked) {
 #pragma unroll
       for (int gi = 0; gi < GPL; ++gi) unpack_group<QF>(tw.c[0][gi], b[gi]);
