@@ -375,7 +375,7 @@ def verify_and_stack(args, dev):
 
 
 def cpu_baseline(spec, ld):
-    """The oracle (float64 NumPy) on decode tokens of the same layer, for about 15 s."""
+    """The oracle (float64 NumPy) on decode tokens of the same layer, for about 12 s (at most 256 tokens)."""
     import synth
     from oracle import moe_oracle as mo
     try:
@@ -383,10 +383,10 @@ def cpu_baseline(spec, ld):
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
-    x = synth.gen_x(spec, seed=0, tokens=64).values
+    x = synth.gen_x(spec, seed=0, tokens=256).values
     t0 = time.time()
     n = 0
-    while n < 64 and (time.time() - t0 < 15.0 or n < 2):
+    while n < 256 and (time.time() - t0 < 12.0 or n < 2):
         mo.layer_forward(ld, x[n:n + 1], keep_expert_out=False)
         n += 1
     dt = time.time() - t0
