@@ -580,3 +580,36 @@ def test_split_expert_calls_match_ffn(T):
     assert np.array_equal(hs.float().cpu().numpy(), g["shared_h"])
     assert np.array_equal(o.cpu().numpy(), g["expert_out"])
     assert np.array_equal(so.cpu().numpy(), g["shared_out"])
+
+
+def test_bound_calls_match_the_wrappers(family1):
+    """api.Bound calls (arguments checked and marshalled once, as bench.py's timed loops use them) give the
+    bits of the checked wrappers: decode steps through moe_layer_forward, and moe_expert_gate_up_q."""
+    ld, L = family1
+    spec = synth.SPECS["decode"]
+    K, E, I = spec.top_k, spec.n_experts, spec.inter
+    xd = gu.x_dev(synth.gen_x(spec, tokens=3), spec.act)
+    ws = api.workspace(L, 1, gu.DEV)
+    y0 = torch.zeros((3, spec.hidden), dtype=torch.float32, device=gu.DEV)
+    y1 = torch.zeros_like(y0)
+    for t in range(3):
+        api.moe_layer_forward(L, xd[t:t + 1], 1, y0[t:t + 1], ws=ws)
+    bound = [api.bind_layer_forward(L, xd[t:t + 1], 1, y1[t:t + 1], ws=ws) for t in range(3)]
+    for _ in range(2):
+        for b in bound:
+            b()
+    ids = torch.empty((1, K), dtype=torch.int32, device=gu.DEV)
+    w = torch.empty((1, K), dtype=torch.float32, device=gu.DEV)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=gu.DEV)
+    sp = torch.empty(K, dtype=torch.int32, device=gu.DEV)
+    pp = torch.empty(K, dtype=torch.int32, device=gu.DEV)
+    api.moe_router_topk(L, xd[:1], 1, ids, w, ws=ws)
+    api.moe_permute(L, ids, 1, offs, sp, pp, ws)
+    h0, h1 = (torch.zeros((K, I), dtype=torch.bfloat16, device=gu.DEV) for _ in range(2))
+    hs0, hs1 = (torch.zeros((1, I), dtype=torch.bfloat16, device=gu.DEV) for _ in range(2))
+    api.moe_expert_gate_up_q(L, xd[:1], 1, ids, offs, sp, h0, hs0)
+    api.bind_expert_gate_up_q(L, xd[:1], 1, ids, offs, sp, h1, hs1)()
+    torch.cuda.synchronize()
+    assert np.array_equal(y0.cpu().numpy(), y1.cpu().numpy())
+    assert torch.equal(h0.view(torch.int16), h1.view(torch.int16)) and torch.equal(hs0.view(torch.int16),
+                                                                                    hs1.view(torch.int16))
