@@ -35,7 +35,10 @@ __device__ __forceinline__ int id_bits(int E) {
 
 // One wave scatters pairs [p0, p1) in order; running[e] holds the next free
 // sorted position of expert e (LDS, owned by this wave).  The ids of 16
-// rounds of 64 pairs are requested together, before the first round.
+// rounds of 64 pairs are requested together, before the first round.  The
+// caller is a one-wave block: the wave's LDS accesses complete in order, so a
+// round's reads of running[] come before its update without a barrier (a block
+// barrier would also wait for the round's global stores).
 __device__ void scatter_chunk(const PermuteArgs& a, int* running, int p0, int p1, int lane, int nbits) {
   constexpr int kRounds = 16;
   for (int b0 = p0; b0 < p1; b0 += 64 * kRounds) {
@@ -57,13 +60,12 @@ __device__ void scatter_chunk(const PermuteArgs& a, int* running, int p0, int p1
       const int cnt = __popcll(same);
       int pos = 0;
       if (valid) pos = running[e] + rank;
-      __syncthreads();
       if (valid) {
         a.sorted_pairs[pos] = p;
         a.pair_pos[p] = pos;
-        if (rank == 0) running[e] += cnt;
+        if (rank == 0) running[e] = pos + cnt;
       }
-      __syncthreads();
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(1024) void k_perm_scan(PermuteArgs a, int n_chunks)
   const int e0 = tid * per;
   // the chunk counts go through in batches of kBatch, all loaded before any is
   // stored, so that the loads of a batch are in flight together
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 32;
   int sum = 0;
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
