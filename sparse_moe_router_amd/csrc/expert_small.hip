@@ -189,6 +189,9 @@ __global__ __launch_bounds__(256) void k_down_sb(FfnArgs a, int ny) {
 bool gateup_sb_ok(const FfnArgs& a) {
   return a.T > 1 && a.T * a.K <= kSbMaxPairs && a.act == MOE_ACT_BF16 && a.H <= 64 * kGroup;
 }
+// I <= 32 groups: k_down_sb stages one (token, group) item of h per thread
+// and chunk (kSbTok tokens x 32 groups = its 256 threads)
+static_assert(kSbTok * 32 <= 256, "one h item per thread and chunk");
 bool down_sb_ok(const FfnArgs& a) {
   return a.T > 1 && a.T * a.K <= kSbMaxPairs && a.act == MOE_ACT_BF16 && a.I <= 32 * kGroup;
 }
