@@ -40,6 +40,17 @@ def round_act(v: float, act: str) -> float:
     return to_bf16(v) if act == "bf16" else to_f32(v)
 
 
+def code3(codes_row, col: int) -> int:
+    """3-bit code of column ``col``: group col // 32 is 12 bytes, 8 of two-bit
+    fields (element 4j+i of the group at bits 2i, 2i+1 of byte j) then 4 of
+    single bits (element i at bit i % 8 of byte 8 + i // 8)."""
+    base = 12 * (col // 32)
+    i = col % 32
+    low = (int(codes_row[base + i // 4]) >> (2 * (i % 4))) & 3
+    high = (int(codes_row[base + 8 + i // 8]) >> (i % 8)) & 1
+    return low | (high << 2)
+
+
 def weight(codes_row, scales_row, mins_row, qfmt: str, col: int) -> float:
     """Dequantised weight at column ``col`` of one packed row."""
     grp = col // 32
@@ -48,6 +59,8 @@ def weight(codes_row, scales_row, mins_row, qfmt: str, col: int) -> float:
         byte = int(codes_row[col // 2])
         u = (byte >> 4) if (col % 2) else (byte & 15)
         return s * (u - 8)
+    if qfmt == "q3_sym_g32":
+        return s * (code3(codes_row, col) - 4)
     byte = int(codes_row[col // 4])
     u = (byte >> (2 * (col % 4))) & 3
     return to_f32(s * u + f16(mins_row[grp]))
@@ -64,6 +77,8 @@ def row_weights(codes_row, scales_row, mins_row, qfmt: str, cols: int):
                 byte = int(codes_row[col // 2])
                 u = (byte >> 4) if (col % 2) else (byte & 15)
                 out.append(s * (u - 8))
+            elif qfmt == "q3_sym_g32":
+                out.append(s * (code3(codes_row, col) - 4))
             else:
                 byte = int(codes_row[col // 4])
                 u = (byte >> (2 * (col % 4))) & 3

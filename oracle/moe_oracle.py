@@ -36,6 +36,7 @@ import numpy as np
 GROUP = 32
 Q4 = "q4_sym_g32"
 Q2 = "q2_asym_g32"
+Q3 = "q3_sym_g32"
 ACT_F32 = "f32"
 ACT_BF16 = "bf16"
 
@@ -71,7 +72,10 @@ def fp16_to_f64(bits):
 
 # ----------------------------------------------------------------------------
 # dequantisation of the group-32 formats (page 1 "Quantization Configuration
-# Example": symmetric grouped 4-bit; page 3: 2-bit)
+# Example": symmetric grouped 4-bit; page 3: 2-bit; page 4 "In brief -- 5 key
+# takeaways" and page 5 "A sensible 4090 setup": a 3-bit quality tier, whose
+# codebook formats the pages do not give -- a plain symmetric 3-bit group-32
+# format stands in for it)
 
 def unpack_q4(codes):
     """uint8 [..., C/2] -> codes u in 0..15, [..., C]; element 2j is the low nibble of byte j."""
@@ -89,6 +93,24 @@ def unpack_q2(codes):
     for i in range(4):
         u[..., i::4] = (c >> (2 * i)) & 3
     return u
+
+
+def unpack_q3(codes):
+    """uint8 [..., 3C/8] -> codes u in 0..7, [..., C].
+
+    Each 32-element group occupies 12 consecutive bytes: bytes 0..7 hold the
+    low two bits of the codes in the 2-bit layout (element 4j+i at bits
+    2i+1..2i of byte j), bytes 8..11 the third bit (element i at bit i mod 8
+    of byte 8 + i div 8); u = low + 4 high.
+    """
+    c = np.asarray(codes, dtype=np.uint8)
+    g = c.reshape(c.shape[:-1] + (c.shape[-1] // 12, 12))
+    low = unpack_q2(g[..., :8])                    # [..., G, 32]
+    high = np.empty_like(low)
+    for i in range(32):
+        high[..., i] = (g[..., 8 + i // 8] >> (i % 8)) & 1
+    u = low + 4 * high
+    return u.reshape(c.shape[:-1] + (u.shape[-2] * 32,))
 
 
 def _per_group(plane, cols):
@@ -109,9 +131,17 @@ def dequant_q2(codes, scales, mins):
     return round_f32(_per_group(scales, cols) * u.astype(np.float64) + _per_group(mins, cols))
 
 
+def dequant_q3(codes, scales):
+    """w = s * (u - 4): exact in float64 and representable in float32 (11-bit x 3-bit)."""
+    u = unpack_q3(codes)
+    return _per_group(scales, u.shape[-1]) * (u - 4).astype(np.float64)
+
+
 def dequant(codes, scales, mins, qfmt):
     if qfmt == Q4:
         return dequant_q4(codes, scales)
+    if qfmt == Q3:
+        return dequant_q3(codes, scales)
     if qfmt == Q2:
         return dequant_q2(codes, scales, mins)
     raise ValueError(qfmt)
@@ -282,22 +312,29 @@ def residual_step(x, y):
 # ----------------------------------------------------------------------------
 # helpers for comparing against an fp32 implementation of the router
 
-def router_error_bound(x, w_r, b):
-    """beta[t,e] = gamma_{3H+1} ((1 + 2^-6) sum_i |W_r[e,i] x[t,i]| + |b_e|),
-    gamma_n = n u / (1 - n u), u = 2^-24.
+def router_error_bound(x, w_r, b, parts=1):
+    """beta[t,e] = gamma_n (c sum_i |W_r[e,i] x[t,i]| + |b_e|), gamma_n = n u / (1 - n u), u = 2^-24.
 
     Worst-case bound on the error of an fp32 evaluation of the logit with exact
-    (float64-representable) inputs, in any summation order: either an fp32 dot
-    product of length H plus the bias, or the sum of 3 H exact products of x
-    with the three bf16 parts of each fp32 weight (hi + mid + lo = w exactly,
-    |hi| + |mid| + |lo| <= (1 + 2^-6) |w|) plus the bias.  The second form
-    has more terms, so its bound covers the first.
+    (float64-representable) inputs, in any summation order, for two forms of
+    the evaluation:
+
+    * ``parts=1``: an fp32 dot product of length H plus the bias: n = H + 1,
+      c = 1 (each product is exact in fp32 or rounded once, each of the H
+      additions rounds once);
+    * ``parts=3``: each fp32 weight split exactly into three bf16 parts
+      (hi + mid + lo = w, |hi| + |mid| + |lo| <= (1 + 2^-6) |w|), the 3 H exact
+      products of x with the parts summed in fp32, plus the bias:
+      n = 3 H + 1, c = 1 + 2^-6.
     """
+    if parts not in (1, 3):
+        raise ValueError(parts)
     hdim = np.asarray(x).shape[-1]
-    n = 3 * hdim + 1
+    n = parts * hdim + 1
     u = 2.0 ** -24
     gamma = n * u / (1 - n * u)
-    mag = (1.0 + 2.0 ** -6) * (np.abs(np.asarray(x, np.float64)) @ np.abs(np.asarray(w_r, np.float64)).T)
+    c = 1.0 if parts == 1 else 1.0 + 2.0 ** -6
+    mag = c * (np.abs(np.asarray(x, np.float64)) @ np.abs(np.asarray(w_r, np.float64)).T)
     if b is not None:
         mag = mag + np.abs(np.asarray(b, np.float64))[None, :]
     return gamma * mag

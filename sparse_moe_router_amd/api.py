@@ -17,9 +17,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_E_ARG, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_DEVICE = range(5)
-MOE_Q4_SYM_G32, MOE_Q2_ASYM_G32 = 1, 2
+MOE_Q4_SYM_G32, MOE_Q2_ASYM_G32, MOE_Q3_SYM_G32 = 1, 2, 3
 MOE_ACT_F32, MOE_ACT_BF16 = 0, 1
-QFMT = {"q4_sym_g32": MOE_Q4_SYM_G32, "q2_asym_g32": MOE_Q2_ASYM_G32}
+QFMT = {"q4_sym_g32": MOE_Q4_SYM_G32, "q2_asym_g32": MOE_Q2_ASYM_G32, "q3_sym_g32": MOE_Q3_SYM_G32}
+CODE_BITS = {MOE_Q4_SYM_G32: 4, MOE_Q3_SYM_G32: 3, MOE_Q2_ASYM_G32: 2}
 ACT = {"f32": MOE_ACT_F32, "bf16": MOE_ACT_BF16}
 
 EXPORTS = ("moe_router_topk", "moe_permute", "moe_expert_ffn_q", "moe_expert_gate_up_q", "moe_expert_down_q",
@@ -91,13 +92,32 @@ def _check(fn: str, status: int):
         raise MoeError(fn, status, lib().moe_status_str(status).decode())
 
 
-def _ptr(t: Optional[torch.Tensor], dtype=None, device_only=True) -> Optional[int]:
+def _need(name: str, t: Optional[torch.Tensor], n: int, dtype=None):
+    """Type, dtype and size of one argument: at least ``n`` elements.
+
+    Checked for every buffer before anything is marshalled: the C ABI receives
+    bare pointers, so a buffer that is too small would turn into a device
+    access out of bounds."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.numel() < n:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {n} needed")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, device=None) -> Optional[int]:
+    """Device address of a contiguous tensor (on ``device`` when given)."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"expected a torch.Tensor, got {type(t).__name__}")
-    if device_only and not t.is_cuda:
+    if not t.is_cuda:
         raise ValueError("tensor must live in device memory")
+    if device is not None and t.device != device:
+        raise ValueError(f"tensor on {t.device}, the layer's weights on {device}")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -132,12 +152,16 @@ class Layer:
         self.act = ACT.get(act, act)
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self.act_dtype = _act_dtype(self.act)
+        self.device = router_w.device
         self._keep = [router_w, router_b, routed, shared]
         if router_w.shape != (n_experts, hidden):
             raise ValueError("router_w must be [E][H]")
         if router_b is not None and router_b.shape != (n_experts,):
             raise ValueError("router_b must be [E]")
-        cb = 4 if self.qfmt == MOE_Q4_SYM_G32 else 2
+        if self.qfmt not in CODE_BITS:
+            raise ValueError(f"unknown format {qfmt!r}")
+        cb = CODE_BITS[self.qfmt]
+        dev = self.device
 
         def qm(parts, n, rows, cols):
             codes, scales, mins = parts
@@ -145,11 +169,11 @@ class Layer:
                 raise ValueError(f"codes must be uint8 [{n}][{rows}][{cols * cb // 8}], got {codes.dtype} {tuple(codes.shape)}")
             if scales.element_size() != 2 or tuple(scales.shape) != (n, rows, cols // 32):
                 raise ValueError("scales must be 16-bit [n][rows][cols/32]")
-            if (mins is None) != (self.qfmt == MOE_Q4_SYM_G32):
+            if (mins is None) != (self.qfmt != MOE_Q2_ASYM_G32):
                 raise ValueError("mins are required for the 2-bit format only")
             if mins is not None and (mins.element_size() != 2 or tuple(mins.shape) != (n, rows, cols // 32)):
                 raise ValueError("mins must be 16-bit [n][rows][cols/32]")
-            return c_qmat(_ptr(codes), _ptr(scales), _ptr(mins))
+            return c_qmat(_ptr(codes, device=dev), _ptr(scales, device=dev), _ptr(mins, device=dev))
 
         def ex(d, n):
             if d is None:
@@ -158,7 +182,7 @@ class Layer:
                              qm(d["down"], n, hidden, inter), n)
 
         self.c = c_layer(hidden, inter, n_experts, top_k, self.qfmt, self.act,
-                         _ptr(router_w, torch.float32), _ptr(router_b, torch.float32),
+                         _ptr(router_w, torch.float32), _ptr(router_b, torch.float32, dev),
                          ex(routed, n_experts), ex(shared, 1))
 
     @property
@@ -178,46 +202,71 @@ def workspace(layer: Layer, T_max: int, device=None) -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 
 
-def _ws(ws):
-    return (None, 0) if ws is None else (_ptr(ws, torch.uint8), ws.numel())
+def _ws(layer: Layer, ws):
+    return (None, 0) if ws is None else (_ptr(ws, torch.uint8, layer.device), ws.numel())
 
 
 def _x(layer: Layer, x: torch.Tensor, T: int):
-    if x.dtype != layer.act_dtype or x.dim() != 2 or x.shape[1] != layer.hidden or x.shape[0] < T:
+    if not isinstance(x, torch.Tensor) or x.dtype != layer.act_dtype or x.dim() != 2 or \
+            x.shape[1] != layer.hidden or x.shape[0] < T:
         raise ValueError(f"x must be {layer.act_dtype} [>=T][{layer.hidden}]")
-    return _ptr(x)
+    return _ptr(x, device=layer.device)
+
+
+def _p(layer: Layer, t, dtype=None):
+    return _ptr(t, dtype, layer.device)
 
 
 def moe_router_topk(layer: Layer, x, T, topk_ids, topk_w, logits=None, ws=None, stream=None):
-    w, wn = _ws(ws)
-    _check("moe_router_topk", lib().moe_router_topk(layer.ref, _x(layer, x, T), int(T), _ptr(topk_ids, torch.int32),
-                                                    _ptr(topk_w, torch.float32), _ptr(logits, torch.float32), w, wn,
-                                                    _stream(stream)))
+    K, E = layer.top_k, layer.n_experts
+    _need("topk_ids", topk_ids, T * K, torch.int32)
+    _need("topk_w", topk_w, T * K, torch.float32)
+    _need("logits", logits, T * E, torch.float32)
+    w, wn = _ws(layer, ws)
+    _check("moe_router_topk", lib().moe_router_topk(layer.ref, _x(layer, x, T), int(T), _p(layer, topk_ids),
+                                                    _p(layer, topk_w), _p(layer, logits), w, wn, _stream(stream)))
 
 
 def moe_permute(layer: Layer, topk_ids, T, expert_offsets, sorted_pairs, pair_pos, ws, stream=None):
-    w, wn = _ws(ws)
-    _check("moe_permute", lib().moe_permute(layer.ref, _ptr(topk_ids, torch.int32), int(T),
-                                            _ptr(expert_offsets, torch.int32), _ptr(sorted_pairs, torch.int32),
-                                            _ptr(pair_pos, torch.int32), w, wn, _stream(stream)))
+    K, E = layer.top_k, layer.n_experts
+    _need("topk_ids", topk_ids, T * K, torch.int32)
+    _need("expert_offsets", expert_offsets, E + 1, torch.int32)
+    _need("sorted_pairs", sorted_pairs, T * K, torch.int32)
+    _need("pair_pos", pair_pos, T * K, torch.int32)
+    w, wn = _ws(layer, ws)
+    _check("moe_permute", lib().moe_permute(layer.ref, _p(layer, topk_ids), int(T), _p(layer, expert_offsets),
+                                            _p(layer, sorted_pairs), _p(layer, pair_pos), w, wn, _stream(stream)))
+
+
+def _routing_inputs(layer: Layer, T, topk_ids, expert_offsets, sorted_pairs):
+    K, E = layer.top_k, layer.n_experts
+    _need("topk_ids", topk_ids, T * K, torch.int32)
+    _need("expert_offsets", expert_offsets, E + 1, torch.int32)
+    _need("sorted_pairs", sorted_pairs, T * K, torch.int32)
 
 
 def moe_expert_ffn_q(layer: Layer, x, T, topk_ids, expert_offsets, sorted_pairs, expert_out, shared_out=None,
                      h=None, shared_h=None, ws=None, stream=None):
-    w, wn = _ws(ws)
-    _check("moe_expert_ffn_q", lib().moe_expert_ffn_q(layer.ref, _x(layer, x, T), int(T), _ptr(topk_ids, torch.int32),
-                                                      _ptr(expert_offsets, torch.int32),
-                                                      _ptr(sorted_pairs, torch.int32),
-                                                      _ptr(expert_out, torch.float32),
-                                                      _ptr(shared_out, torch.float32),
-                                                      _ptr(h, layer.act_dtype), _ptr(shared_h, layer.act_dtype),
-                                                      w, wn, _stream(stream)))
+    K, H, I = layer.top_k, layer.hidden, layer.inter
+    _routing_inputs(layer, T, topk_ids, expert_offsets, sorted_pairs)
+    _need("expert_out", expert_out, T * K * H, torch.float32)
+    _need("shared_out", shared_out, T * H, torch.float32)
+    _need("h", h, T * K * I, layer.act_dtype)
+    _need("shared_h", shared_h, T * I, layer.act_dtype)
+    w, wn = _ws(layer, ws)
+    _check("moe_expert_ffn_q", lib().moe_expert_ffn_q(layer.ref, _x(layer, x, T), int(T), _p(layer, topk_ids),
+                                                      _p(layer, expert_offsets), _p(layer, sorted_pairs),
+                                                      _p(layer, expert_out), _p(layer, shared_out), _p(layer, h),
+                                                      _p(layer, shared_h), w, wn, _stream(stream)))
 
 
 def _gate_up_args(layer, x, T, topk_ids, expert_offsets, sorted_pairs, h, shared_h, stream):
-    return (layer.ref, _x(layer, x, T), int(T), _ptr(topk_ids, torch.int32), _ptr(expert_offsets, torch.int32),
-            _ptr(sorted_pairs, torch.int32), _ptr(h, layer.act_dtype), _ptr(shared_h, layer.act_dtype),
-            _stream(stream))
+    K, I = layer.top_k, layer.inter
+    _routing_inputs(layer, T, topk_ids, expert_offsets, sorted_pairs)
+    _need("h", h, T * K * I, layer.act_dtype)
+    _need("shared_h", shared_h, T * I, layer.act_dtype)
+    return (layer.ref, _x(layer, x, T), int(T), _p(layer, topk_ids), _p(layer, expert_offsets),
+            _p(layer, sorted_pairs), _p(layer, h), _p(layer, shared_h), _stream(stream))
 
 
 def moe_expert_gate_up_q(layer: Layer, x, T, topk_ids, expert_offsets, sorted_pairs, h, shared_h=None,
@@ -228,28 +277,42 @@ def moe_expert_gate_up_q(layer: Layer, x, T, topk_ids, expert_offsets, sorted_pa
 
 def moe_expert_down_q(layer: Layer, h, shared_h, T, topk_ids, expert_offsets, sorted_pairs, expert_out,
                       shared_out=None, stream=None):
-    _check("moe_expert_down_q", lib().moe_expert_down_q(layer.ref, _ptr(h, layer.act_dtype),
-                                                        _ptr(shared_h, layer.act_dtype), int(T),
-                                                        _ptr(topk_ids, torch.int32),
-                                                        _ptr(expert_offsets, torch.int32),
-                                                        _ptr(sorted_pairs, torch.int32),
-                                                        _ptr(expert_out, torch.float32),
-                                                        _ptr(shared_out, torch.float32), _stream(stream)))
+    K, H, I = layer.top_k, layer.hidden, layer.inter
+    _routing_inputs(layer, T, topk_ids, expert_offsets, sorted_pairs)
+    _need("h", h, T * K * I, layer.act_dtype)
+    _need("shared_h", shared_h, T * I, layer.act_dtype)
+    _need("expert_out", expert_out, T * K * H, torch.float32)
+    _need("shared_out", shared_out, T * H, torch.float32)
+    _check("moe_expert_down_q", lib().moe_expert_down_q(layer.ref, _p(layer, h), _p(layer, shared_h), int(T),
+                                                        _p(layer, topk_ids), _p(layer, expert_offsets),
+                                                        _p(layer, sorted_pairs), _p(layer, expert_out),
+                                                        _p(layer, shared_out), _stream(stream)))
 
 
 def moe_combine(layer: Layer, expert_out, shared_out, pair_pos, topk_w, T, y, x_resid=None, x_next=None,
                 stream=None):
-    _check("moe_combine", lib().moe_combine(layer.ref, _ptr(expert_out, torch.float32),
-                                            _ptr(shared_out, torch.float32), _ptr(pair_pos, torch.int32),
-                                            _ptr(topk_w, torch.float32), int(T), _ptr(y, torch.float32),
-                                            _ptr(x_resid, layer.act_dtype), _ptr(x_next, layer.act_dtype),
-                                            _stream(stream)))
+    K, H = layer.top_k, layer.hidden
+    _need("expert_out", expert_out, T * K * H, torch.float32)
+    _need("shared_out", shared_out, T * H, torch.float32)
+    _need("pair_pos", pair_pos, T * K, torch.int32)
+    _need("topk_w", topk_w, T * K, torch.float32)
+    _need("y", y, T * H, torch.float32)
+    _need("x_resid", x_resid, T * H, layer.act_dtype)
+    _need("x_next", x_next, T * H, layer.act_dtype)
+    _check("moe_combine", lib().moe_combine(layer.ref, _p(layer, expert_out), _p(layer, shared_out),
+                                            _p(layer, pair_pos), _p(layer, topk_w), int(T), _p(layer, y),
+                                            _p(layer, x_resid), _p(layer, x_next), _stream(stream)))
 
 
 def _layer_forward_args(layer, x, T, y, x_next, topk_ids, topk_w, ws, stream):
-    w, wn = _ws(ws)
-    return (layer.ref, _x(layer, x, T), int(T), _ptr(y, torch.float32), _ptr(x_next, layer.act_dtype),
-            _ptr(topk_ids, torch.int32), _ptr(topk_w, torch.float32), w, wn, _stream(stream))
+    K, H = layer.top_k, layer.hidden
+    _need("y", y, T * H, torch.float32)
+    _need("x_next", x_next, T * H, layer.act_dtype)
+    _need("topk_ids", topk_ids, T * K, torch.int32)
+    _need("topk_w", topk_w, T * K, torch.float32)
+    w, wn = _ws(layer, ws)
+    return (layer.ref, _x(layer, x, T), int(T), _p(layer, y), _p(layer, x_next), _p(layer, topk_ids),
+            _p(layer, topk_w), w, wn, _stream(stream))
 
 
 def moe_layer_forward(layer: Layer, x, T, y, x_next=None, topk_ids=None, topk_w=None, ws=None, stream=None):
@@ -292,17 +355,30 @@ def bind_expert_gate_up_q(layer: Layer, x, T, topk_ids, expert_offsets, sorted_p
 
 def moe_stack_forward(layers, x_inout, T, y_last=None, ws=None, stream=None):
     arr = (c_layer * len(layers))(*[l.c for l in layers])
-    w, wn = _ws(ws)
-    if layers:
-        _x(layers[0], x_inout, T)
-    _check("moe_stack_forward", lib().moe_stack_forward(arr, len(layers), _ptr(x_inout), int(T),
-                                                        _ptr(y_last, torch.float32), w, wn, _stream(stream)))
+    if not layers:
+        _check("moe_stack_forward", lib().moe_stack_forward(arr, 0, None, int(T), None, None, 0, _stream(stream)))
+        return
+    L0 = layers[0]
+    if any(l.device != L0.device for l in layers):
+        raise ValueError("every layer of a stack must live on one device")
+    _need("y_last", y_last, T * L0.hidden, torch.float32)
+    w, wn = _ws(L0, ws)
+    _check("moe_stack_forward", lib().moe_stack_forward(arr, len(layers), _x(L0, x_inout, T), int(T),
+                                                        _p(L0, y_last), w, wn, _stream(stream)))
 
 
 def moe_dequant(codes, scales, mins, qfmt, rows, cols, out, stream=None):
-    m = c_qmat(_ptr(codes), _ptr(scales), _ptr(mins))
-    _check("moe_dequant", lib().moe_dequant(ctypes.byref(m), QFMT.get(qfmt, qfmt), int(rows), int(cols),
-                                            _ptr(out, torch.float32), _stream(stream)))
+    q = QFMT.get(qfmt, qfmt)
+    if q not in CODE_BITS:
+        raise ValueError(f"unknown format {qfmt!r}")
+    _need("codes", codes, rows * cols * CODE_BITS[q] // 8, torch.uint8)
+    _need("scales", scales, rows * (cols // 32))
+    _need("mins", mins, rows * (cols // 32))
+    _need("out", out, rows * cols, torch.float32)
+    dev = out.device
+    m = c_qmat(_ptr(codes, device=dev), _ptr(scales, device=dev), _ptr(mins, device=dev))
+    _check("moe_dequant", lib().moe_dequant(ctypes.byref(m), q, int(rows), int(cols), _ptr(out, torch.float32),
+                                            _stream(stream)))
 
 
 def moe_abi_version() -> int:

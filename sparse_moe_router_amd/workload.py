@@ -11,7 +11,7 @@ GROUP = 32
 
 
 def code_bits(qfmt: str) -> int:
-    return {"q4_sym_g32": 4, "q2_asym_g32": 2}[qfmt]
+    return {"q4_sym_g32": 4, "q3_sym_g32": 3, "q2_asym_g32": 2}[qfmt]
 
 
 def matrix_bytes(qfmt: str, rows: int, cols: int) -> int:

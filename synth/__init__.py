@@ -30,6 +30,7 @@ import numpy as np
 
 Q4 = "q4_sym_g32"
 Q2 = "q2_asym_g32"
+Q3 = "q3_sym_g32"
 ACT_F32 = "f32"
 ACT_BF16 = "bf16"
 GROUP = 32
@@ -106,8 +107,10 @@ def f64_to_f16_bits(a: np.ndarray) -> np.ndarray:
 # Groups of 32 consecutive elements run along each matrix's last (reduction)
 # dimension.  Q4: byte j of a row holds element 2j in its low nibble and 2j+1
 # in its high nibble, stored as u = q + 8.  Q2: byte j holds elements
-# 4j..4j+3 in bits [1:0], [3:2], [5:4], [7:6].  Scales and minima are fp16
-# planes [rows][cols/32].
+# 4j..4j+3 in bits [1:0], [3:2], [5:4], [7:6].  Q3: 12 bytes per group, the
+# low two bits of the codes in the Q2 layout (8 bytes), then the third bit of
+# element i at bit i % 8 of byte 8 + i // 8, stored as u = q + 4.  Scales and
+# minima are fp16 planes [rows][cols/32].
 
 def pack_q4(u: np.ndarray) -> np.ndarray:
     u = np.asarray(u, dtype=np.uint8)
@@ -118,6 +121,20 @@ def pack_q2(u: np.ndarray) -> np.ndarray:
     u = np.asarray(u, dtype=np.uint8)
     return ((u[..., 0::4] & 3) | ((u[..., 1::4] & 3) << 2)
             | ((u[..., 2::4] & 3) << 4) | ((u[..., 3::4] & 3) << 6)).astype(np.uint8)
+
+
+def pack_q3(u: np.ndarray) -> np.ndarray:
+    """Codes u in 0..7 [..., C] -> [..., 3C/8]: per 32-element group 12 bytes, the
+    low two bits in the 2-bit layout (bytes 0..7), then the third bit of
+    element i at bit i % 8 of byte 8 + i // 8."""
+    u = np.asarray(u, dtype=np.uint8)
+    g = u.reshape(*u.shape[:-1], u.shape[-1] // GROUP, GROUP)
+    low = pack_q2(g & 3)                                       # [..., G, 8]
+    hb = (g >> 2) & 1
+    high = np.zeros(g.shape[:-1] + (4,), np.uint8)
+    for i in range(GROUP):
+        high[..., i // 8] |= (hb[..., i] << (i % 8)).astype(np.uint8)
+    return np.concatenate([low, high], axis=-1).reshape(*u.shape[:-1], u.shape[-1] * 3 // 8)
 
 
 def quantize_q4(w: np.ndarray):
@@ -135,6 +152,23 @@ def quantize_q4(w: np.ndarray):
     q = np.clip(q, -8, 7).astype(np.int16)
     u = (q + 8).astype(np.uint8).reshape(w.shape)
     return pack_q4(u), s16.view(np.uint16)
+
+
+def quantize_q3(w: np.ndarray):
+    """Symmetric round-to-nearest 3-bit, group 32: s = fp16(amax/3), q = clamp(rint(w/s), -4, 3).
+
+    Returns (codes uint8 [..., 3 cols/8], scales fp16 bits [..., cols/32]).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    g = w.reshape(*w.shape[:-1], w.shape[-1] // GROUP, GROUP).astype(np.float64)
+    amax = np.abs(g).max(axis=-1)
+    s16 = (amax / 3.0).astype(np.float16)
+    s = s16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.rint(g / np.where(s > 0, s, 1.0)), 0.0)
+    q = np.clip(q, -4, 3).astype(np.int16)
+    u = (q + 4).astype(np.uint8).reshape(w.shape)
+    return pack_q3(u), s16.view(np.uint16)
 
 
 def quantize_q2(w: np.ndarray):
@@ -164,6 +198,15 @@ def requantize_codes_q4(w: np.ndarray, scales_bits: np.ndarray) -> np.ndarray:
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.where(s != 0, np.rint(g / np.where(s != 0, s, 1.0)), 0.0)
     return (np.clip(q, -8, 7) + 8).astype(np.uint8).reshape(w.shape)
+
+
+def requantize_codes_q3(w: np.ndarray, scales_bits: np.ndarray) -> np.ndarray:
+    """Codes u in [0,7] that the quantizer picks for weights w under given fp16 scales."""
+    g = np.asarray(w, dtype=np.float64).reshape(*w.shape[:-1], w.shape[-1] // GROUP, GROUP)
+    s = np.asarray(scales_bits, dtype=np.uint16).view(np.float16).astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s != 0, np.rint(g / np.where(s != 0, s, 1.0)), 0.0)
+    return (np.clip(q, -4, 3) + 4).astype(np.uint8).reshape(w.shape)
 
 
 def requantize_codes_q2(w: np.ndarray, scales_bits: np.ndarray, mins_bits: np.ndarray) -> np.ndarray:
@@ -246,6 +289,9 @@ def _quantize(spec: LayerSpec, w: np.ndarray):
         return c, s, None
     if spec.qfmt == Q2:
         return quantize_q2(w)
+    if spec.qfmt == Q3:
+        c, s = quantize_q3(w)
+        return c, s, None
     raise ValueError(spec.qfmt)
 
 
@@ -263,7 +309,7 @@ def _gen_one(spec: LayerSpec, seed: int, layer: int, e: int):
 
 
 def code_bytes_per_row(qfmt: str, cols: int) -> int:
-    return cols // 2 if qfmt == Q4 else cols // 4
+    return {Q4: cols // 2, Q3: cols * 3 // 8, Q2: cols // 4}[qfmt]
 
 
 def _alloc_set(spec: LayerSpec, n: int) -> ExpertSet:

@@ -45,10 +45,10 @@ def device_filled_kwargs(spec, layer: int, device, seed: int = 0) -> dict:
     codes, fp16 scales s = 0.0274 U(0.85, 1.15) and, for the 2-bit format,
     minima m = -1.5 s (the stand-in expert distribution of the stack recipe);
     the router and its bias come from gen_router as for every other layer."""
-    from . import Q2, gen_router
+    from . import Q2, Q3, gen_router
     g = torch.Generator(device=device)
     g.manual_seed((seed * 1_000_003 + spec.family * 10_007 + layer) & 0x7FFFFFFF)
-    bits = 2 if spec.qfmt == Q2 else 4
+    bits = {Q2: 2, Q3: 3}.get(spec.qfmt, 4)
 
     def mat(n, rows, cols):
         codes = torch.randint(0, 256, (n, rows, cols * bits // 8), dtype=torch.uint8, device=device, generator=g)

@@ -68,6 +68,17 @@ def run_forward(L: api.Layer, x: torch.Tensor, T: int, x_next=False):
                 x_next=None if xn is None else xn.cpu())
 
 
+# bf16 activations and at least this many tokens: the library evaluates the
+# logits on the matrix cores with each fp32 weight split into three bf16 parts
+ROUTER_MFMA_MIN_TOKENS = 32
+
+
+def router_parts(spec, T):
+    """Parts per weight of the library's logit evaluation for a call of T tokens:
+    3 on the matrix-core path (bf16 x, T >= 32), else 1 (an fp32 dot product)."""
+    return 3 if spec.act == synth.ACT_BF16 and T >= ROUTER_MFMA_MIN_TOKENS else 1
+
+
 def check_routing(ld: synth.LayerData, xv: np.ndarray, gpu: dict, tokens=None):
     """Router logits within the fp32 bound, ids identical to the oracle's
     selection on the GPU's own fp32 logits, and identical (or a certified
@@ -76,7 +87,7 @@ def check_routing(ld: synth.LayerData, xv: np.ndarray, gpu: dict, tokens=None):
     spec = ld.spec
     tok = np.arange(xv.shape[0]) if tokens is None else np.asarray(tokens)
     exact = mo.router_logits(xv[tok], ld.router_w, ld.router_b)
-    beta = mo.router_error_bound(xv[tok], ld.router_w, ld.router_b)
+    beta = mo.router_error_bound(xv[tok], ld.router_w, ld.router_b, parts=router_parts(spec, xv.shape[0]))
     lg = gpu["logits"][tok].astype(np.float64)
     assert np.all(np.abs(lg - exact) <= beta), "router logits outside the fp32 error bound"
     ids_gpu = gpu["ids"][tok]

@@ -152,3 +152,91 @@ def test_bound_call_reports_the_status():
     good = layer()
     api.Bound("moe_layer_forward", (ctypes.byref(good), None, 0, None, None, None, None, None, 0, None),
               keep=(good,))()
+
+
+# ----------------------------------------------------------------------------- binding argument sizes
+
+def fake_layer(T_hidden=64, inter=96, E=8, K=3, act=api.MOE_ACT_BF16):
+    """A binding-level Layer without device tensors: only the fields the wrappers' checks read."""
+    import torch
+    L = object.__new__(api.Layer)
+    L.hidden, L.inter, L.n_experts, L.top_k = T_hidden, inter, E, K
+    L.act, L.qfmt = act, api.MOE_Q4_SYM_G32
+    L.act_dtype = torch.bfloat16 if act == api.MOE_ACT_BF16 else torch.float32
+    L.device = torch.device("cuda", 0)
+    L.c = layer(hidden=T_hidden, inter=inter, n_experts=E, top_k=K)
+    return L
+
+
+def binding_calls(L, T):
+    """(name, call(args), args) of every wrapper with correctly sized host tensors."""
+    import torch
+    K, E, H, I = L.top_k, L.n_experts, L.hidden, L.inter
+    a, i32, f32 = L.act_dtype, torch.int32, torch.float32
+    z = lambda n, d: torch.zeros(n, dtype=d)
+    x = torch.zeros((T, H), dtype=a)
+    return [
+        ("moe_router_topk", lambda d: api.moe_router_topk(L, x, T, d["topk_ids"], d["topk_w"], d["logits"]),
+         dict(topk_ids=z(T * K, i32), topk_w=z(T * K, f32), logits=z(T * E, f32))),
+        ("moe_permute", lambda d: api.moe_permute(L, d["topk_ids"], T, d["expert_offsets"], d["sorted_pairs"],
+                                                  d["pair_pos"], None),
+         dict(topk_ids=z(T * K, i32), expert_offsets=z(E + 1, i32), sorted_pairs=z(T * K, i32),
+              pair_pos=z(T * K, i32))),
+        ("moe_expert_ffn_q", lambda d: api.moe_expert_ffn_q(L, x, T, d["topk_ids"], d["expert_offsets"],
+                                                            d["sorted_pairs"], d["expert_out"], d["shared_out"],
+                                                            d["h"], d["shared_h"]),
+         dict(topk_ids=z(T * K, i32), expert_offsets=z(E + 1, i32), sorted_pairs=z(T * K, i32),
+              expert_out=z(T * K * H, f32), shared_out=z(T * H, f32), h=z(T * K * I, a), shared_h=z(T * I, a))),
+        ("moe_expert_gate_up_q", lambda d: api.moe_expert_gate_up_q(L, x, T, d["topk_ids"], d["expert_offsets"],
+                                                                    d["sorted_pairs"], d["h"], d["shared_h"]),
+         dict(topk_ids=z(T * K, i32), expert_offsets=z(E + 1, i32), sorted_pairs=z(T * K, i32),
+              h=z(T * K * I, a), shared_h=z(T * I, a))),
+        ("moe_expert_down_q", lambda d: api.moe_expert_down_q(L, d["h"], d["shared_h"], T, d["topk_ids"],
+                                                              d["expert_offsets"], d["sorted_pairs"],
+                                                              d["expert_out"], d["shared_out"]),
+         dict(topk_ids=z(T * K, i32), expert_offsets=z(E + 1, i32), sorted_pairs=z(T * K, i32),
+              h=z(T * K * I, a), shared_h=z(T * I, a), expert_out=z(T * K * H, f32), shared_out=z(T * H, f32))),
+        ("moe_combine", lambda d: api.moe_combine(L, d["expert_out"], d["shared_out"], d["pair_pos"], d["topk_w"],
+                                                  T, d["y"], d["x_resid"], d["x_next"]),
+         dict(expert_out=z(T * K * H, f32), shared_out=z(T * H, f32), pair_pos=z(T * K, i32),
+              topk_w=z(T * K, f32), y=z(T * H, f32), x_resid=z(T * H, a), x_next=z(T * H, a))),
+        ("moe_layer_forward", lambda d: api.moe_layer_forward(L, x, T, d["y"], d["x_next"], d["topk_ids"],
+                                                              d["topk_w"]),
+         dict(y=z(T * H, f32), x_next=z(T * H, a), topk_ids=z(T * K, i32), topk_w=z(T * K, f32))),
+        ("moe_stack_forward", lambda d: api.moe_stack_forward([L], x, T, d["y_last"]),
+         dict(y_last=z(T * H, f32))),
+    ]
+
+
+CALLS = [c[0] for c in binding_calls(fake_layer(), 5)]
+
+
+@pytest.mark.parametrize("name", CALLS)
+def test_binding_rejects_every_undersized_buffer(name):
+    """Each buffer one element short raises ValueError naming it, before any pointer is
+    taken; with every buffer at its size the call gets past the size checks (and then
+    stops at the device check, these being host tensors)."""
+    L = fake_layer()
+    call, args = {n: (c, a) for n, c, a in binding_calls(L, 5)}[name]
+    for key, t in args.items():
+        short = dict(args)
+        short[key] = t[:-1]
+        with pytest.raises(ValueError, match=f"{key}: .* at least {t.numel()} needed"):
+            call(short)
+    with pytest.raises(ValueError, match="device memory"):
+        call(args)
+
+
+def test_binding_checks_dequant_sizes():
+    import torch
+    out = torch.zeros(4 * 64, dtype=torch.float32)
+    for qfmt, cb in (("q4_sym_g32", 4), ("q3_sym_g32", 3), ("q2_asym_g32", 2)):
+        codes = torch.zeros(4 * 64 * cb // 8, dtype=torch.uint8)
+        sc = torch.zeros(8, dtype=torch.int16)
+        mins = sc if qfmt == "q2_asym_g32" else None
+        with pytest.raises(ValueError, match="codes"):
+            api.moe_dequant(codes[:-1], sc, mins, qfmt, 4, 64, out)
+        with pytest.raises(ValueError, match="out"):
+            api.moe_dequant(codes, sc, mins, qfmt, 4, 64, out[:-1])
+        with pytest.raises(ValueError, match="device memory"):
+            api.moe_dequant(codes, sc, mins, qfmt, 4, 64, out)

@@ -39,6 +39,24 @@ MUTATIONS = [
     ("gate_and_up_swapped", "v = silu(g) * u", "v = silu(u) * g"),
     ("h_not_rounded", "h = round_act(v, act)", "h = v"),
     ("shared_expert_dropped", "shared_out = shared_out + sj", "shared_out = shared_out"),
+    ("q3_high_bit_position",
+     "high[..., i] = (g[..., 8 + i // 8] >> (i % 8)) & 1",
+     "high[..., i] = (g[..., 8 + i % 4] >> (i // 4)) & 1"),
+    ("q3_offset", "* (u - 4).astype(np.float64)", "* (u - 3).astype(np.float64)"),
+    ("q3_low_and_high_swapped", "u = low + 4 * high", "u = 2 * low + high"),
+    ("bf16_ties_away_from_zero",
+     "keep = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16) << 16",
+     "keep = ((bits + 0x8000) >> 16) << 16"),
+    ("bf16_single_rounding_from_float64",
+     "    return keep.astype(np.uint32).view(np.float32).astype(np.float64)",
+     "    v = np.asarray(a, np.float64)\n"
+     "    ulp = 2.0 ** (np.floor(np.log2(np.where(v == 0, 1.0, np.abs(v)))) - 7)\n"
+     "    return np.round(v / ulp) * ulp"),
+    ("residual_single_rounding_from_float64",
+     "return round_bf16(round_f32(np.asarray(x, np.float64) + np.asarray(y, np.float64)))",
+     "v = np.asarray(x, np.float64) + np.asarray(y, np.float64)\n"
+     "    ulp = 2.0 ** (np.floor(np.log2(np.where(v == 0, 1.0, np.abs(v)))) - 7)\n"
+     "    return np.round(v / ulp) * ulp"),
     ("combine_slot_shifted",
      "y = y + w[:, kk:kk + 1] * o_tk[:, kk, :]",
      "y = y + w[:, kk:kk + 1] * o_tk[:, (kk + 1) % o_tk.shape[1], :]"),

@@ -29,7 +29,7 @@ def small_spec(rng, qfmt=None, act=None, hidden=None, e=None, k=None, inter=None
     k = k or int(rng.integers(1, e + 1))
     inter = inter or int(rng.choice([32, 64, 128]))
     t = t or int(rng.integers(1, 9))
-    qfmt = qfmt or (synth.Q4 if rng.random() < 0.5 else synth.Q2)
+    qfmt = qfmt or str(rng.choice([synth.Q4, synth.Q3, synth.Q2]))
     act = act or (synth.ACT_F32 if rng.random() < 0.5 else synth.ACT_BF16)
     use_bias = bool(rng.random() < 0.5) if bias is None else bias
     return synth.LayerSpec("rand", hidden, e, k, inter, t, qfmt, act, 0.3, 1.1 if use_bias else None,
@@ -220,6 +220,40 @@ def test_dequant_q2_grid():
         assert got[r].tolist() == want
 
 
+def test_q3_layout_hand_packed_bytes():
+    """The 3-bit layout on bytes written out by hand: codes u_i = i mod 8 give
+    low fields (0, 1, 2, 3) in every low byte (0xE4) and the third bit set for
+    elements 4..7 of every 8 (0xF0); a lone code 7 at element 13 sets bits 2, 3
+    of byte 3 and bit 5 of byte 9."""
+    a = np.array([0xE4] * 8 + [0xF0] * 4, np.uint8)
+    assert mo.unpack_q3(a).tolist() == [i % 8 for i in range(32)]
+    b = np.zeros(12, np.uint8)
+    b[3], b[9] = 0x0C, 0x20
+    want = [0] * 32
+    want[13] = 7
+    assert mo.unpack_q3(b).tolist() == want
+    # two groups per row: the second group's 12 bytes follow the first's
+    assert mo.unpack_q3(np.concatenate([b, a])).tolist() == want + [i % 8 for i in range(32)]
+    assert synth.pack_q3(np.array([i % 8 for i in range(32)], np.uint8)).tolist() == a.tolist()
+
+
+def test_dequant_q3_exhaustive():
+    """Every code x every finite fp16 scale, against struct-decoded halves, and the
+    scalar decoder of the brute-force oracle on random packed rows."""
+    sb = _all_finite_f16_bits()
+    codes_u = np.tile(np.arange(8, dtype=np.uint8), 4)
+    packed = synth.pack_q3(np.tile(codes_u, (sb.size, 1)))
+    got = mo.dequant_q3(packed, sb[:, None])
+    halves = np.array([struct.unpack("<e", struct.pack("<H", int(v)))[0] for v in sb])
+    want = halves[:, None] * (codes_u.astype(np.float64) - 4)[None, :]
+    assert np.array_equal(got, want)
+    assert np.array_equal(got.astype(np.float32).astype(np.float64), got)
+    rng = np.random.default_rng(21)
+    for _ in range(20):
+        row = rng.integers(0, 256, size=12 * 3, dtype=np.uint8)
+        assert mo.unpack_q3(row).tolist() == [bf.code3(row.tolist(), c) for c in range(96)]
+
+
 def test_quantizer_round_trip():
     rng = np.random.default_rng(12)
     for _ in range(20):
@@ -233,6 +267,10 @@ def test_quantizer_round_trip():
         m2 = synth.f64_to_f16_bits(-1.5 * rng.uniform(1e-3, 1.0, size=(rows, 2)))
         w2 = mo.dequant_q2(synth.pack_q2(u2), s2, m2)
         assert np.array_equal(synth.requantize_codes_q2(w2, s2, m2), u2)
+        u3 = rng.integers(0, 8, size=(rows, 64)).astype(np.uint8)
+        s3 = synth.f64_to_f16_bits(rng.uniform(1e-3, 1.0, size=(rows, 2)))
+        w3 = mo.dequant_q3(synth.pack_q3(u3), s3)
+        assert np.array_equal(synth.requantize_codes_q3(w3, s3), u3)
 
 
 def test_quantizer_error_within_half_step():
@@ -242,6 +280,10 @@ def test_quantizer_error_within_half_step():
     d4 = mo.dequant_q4(c4, s4)
     step = np.repeat(s4.view(np.float16).astype(np.float64), 32, -1)
     assert np.all(np.abs(d4 - w) <= 0.5 * step * (1 + 1e-3) + 1e-12)
+    c3, s3 = synth.quantize_q3(w)
+    d3 = mo.dequant_q3(c3, s3)
+    step3 = np.repeat(s3.view(np.float16).astype(np.float64), 32, -1)
+    assert np.all(np.abs(d3 - w) <= 0.5 * step3 * (1 + 1e-3) + 1e-12)
     c2, s2, m2 = synth.quantize_q2(w)
     d2 = mo.dequant_q2(c2, s2, m2)
     step2 = np.repeat(s2.view(np.float16).astype(np.float64), 32, -1)
@@ -280,7 +322,9 @@ def test_expert_relabelling_invariance():
         perm = rng.permutation(spec.n_experts)
         ref2 = mo.layer_forward(_relabel(layer, perm), x)
         assert np.array_equal(ref2["ids"], perm[ref["ids"]])
-        assert np.array_equal(ref2["w"], ref["w"])
+        # exact in exact arithmetic; the float64 router product may round a moved
+        # row differently in the last bit (the BLAS blocking depends on row position)
+        np.testing.assert_allclose(ref2["w"], ref["w"], rtol=1e-14, atol=0)
         np.testing.assert_allclose(ref2["y"], ref["y"], rtol=1e-14, atol=1e-16)
 
 
@@ -349,14 +393,81 @@ def test_hand_worked_layer():
     assert np.allclose(ref["y"], 32 * 1.5 * hs + 32 * 0.25 * h1, rtol=1e-15, atol=0)
 
 
+# ----------------------------------------------------------------------------- rounding points
+
+def _torch_bf16(v32):
+    """torch's CPU float32 -> bfloat16 conversion (round to nearest, ties to even)."""
+    import torch
+    return torch.from_numpy(np.asarray(v32, np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def test_round_bf16_exact_ties_against_torch():
+    """float32 values whose low half is exactly 0x8000 (a tie), with bit 16 even and
+    odd, both signs, normal and subnormal, round to even as torch's conversion does;
+    values one ulp either side of the tie round to the nearer neighbour."""
+    his = np.array([0x3F80, 0x3F81, 0x4049, 0x404A, 0x0001, 0x0002, 0x7F7E, 0x7F7D, 0x0080, 0x3FFF], np.uint32)
+    his = np.concatenate([his, his | 0x8000])
+    ties = ((his << 16) | 0x8000).astype(np.uint32)
+    near = np.concatenate([ties, ties - 1, ties + 1])
+    v = near.view(np.float32)
+    got = mo.round_bf16(v.astype(np.float64))
+    assert np.array_equal(got, _torch_bf16(v).astype(np.float64))
+    # the tie cases written out: even upper halves stay, odd ones go up by one unit
+    t = ties.view(np.float32)
+    want_bits = np.where(his & 1, his + 1, his) << 16
+    assert np.array_equal(got[:ties.size], want_bits.astype(np.uint32).view(np.float32).astype(np.float64))
+    assert np.array_equal(got[:ties.size], np.array([bf.to_bf16(float(a)) for a in t]))
+
+
+def test_round_bf16_goes_through_float32():
+    """The storage rounding of h (and of the residual stream) is fp32 first, then bf16.
+    1 + 2^-8 + 2^-30 lies above the bf16 tie 1 + 2^-8, but its fp32 rounding is the
+    tie itself (2^-30 is below half an fp32 ulp at 1), which then rounds to even:
+    1.0.  A single rounding from float64 would give 1 + 2^-7."""
+    v = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert mo.round_bf16(np.array([v])).tolist() == [1.0]
+    assert mo.round_bf16(np.array([-v])).tolist() == [-1.0]
+    assert bf.to_bf16(v) == 1.0
+    # just above the fp32 half ulp the fp32 value moves off the tie and bf16 rounds up
+    w = 1.0 + 2.0 ** -8 + 2.0 ** -23
+    assert mo.round_bf16(np.array([w])).tolist() == [1.0 + 2.0 ** -7]
+
+
+def test_residual_step_rounds_fp32_then_bf16():
+    """x_next = bf16(fp32(x + y)) with bf16 x and fp32 y, on sums where the two-step
+    rounding differs from one rounding of the exact sum (values worked by hand):
+      1 + fp32(2^-8 + 2^-30)          -> 1.0        (one rounding: 1 + 2^-7)
+      (1 + 2^-7) + 2^-8               -> 1 + 2^-6   (an exact tie, odd -> even, up)
+      256 + fp32(-(2^-1 + 2^-24))     -> 256.0      (fp32 sum is 255.5, a tie, even stays;
+                                                     one rounding: 255.0)
+      -3 + fp32(-2^-7 - 2^-28)        -> -3.0       (fp32 sum is the tie -(3 + 2^-7);
+                                                     one rounding: -3.015625)"""
+    f32 = lambda v: struct.unpack("<f", struct.pack("<f", v))[0]
+    cases = [
+        (1.0, f32(2.0 ** -8 + 2.0 ** -30), 1.0),
+        (1.0 + 2.0 ** -7, 2.0 ** -8, 1.0 + 2.0 ** -6),
+        (256.0, f32(-(2.0 ** -1 + 2.0 ** -24)), 256.0),
+        (-3.0, f32(-(2.0 ** -7 + 2.0 ** -28)), -3.0),
+    ]
+    for x, y, want in cases:
+        assert f32(y) == y
+        assert mo.residual_step(np.array([[x]]), np.array([[y]])).tolist() == [[want]], (x, y)
+
+
 # ----------------------------------------------------------------------------- router bound helpers
 
-def test_router_bound_covers_fp32_evaluation():
-    """An fp32 evaluation of the logits (sequential sum) stays within the stated bound."""
+def _router_case():
     rng = np.random.default_rng(18)
     x = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal((3, 2048)).astype(np.float32)))
     w = (rng.standard_normal((16, 2048)) * 0.022).astype(np.float32)
     b = rng.standard_normal(16).astype(np.float32)
+    return x, w, b
+
+
+def test_router_bound_covers_fp32_evaluation():
+    """An fp32 dot-product evaluation of the logits (sequential sum) stays within
+    the one-part bound gamma_{H+1} (sum |W x| + |b|)."""
+    x, w, b = _router_case()
     exact = mo.router_logits(x, w, b)
     beta = mo.router_error_bound(x, w, b)
     f32 = np.zeros((3, 16), np.float32)
@@ -364,6 +475,31 @@ def test_router_bound_covers_fp32_evaluation():
         f32 = (f32 + x[:, i:i + 1] * w[None, :, i]).astype(np.float32)
     f32 = (f32 + b).astype(np.float32)
     assert np.all(np.abs(f32.astype(np.float64) - exact) <= beta)
+    # the bound is the textbook gamma_{H+1}: 2049 u / (1 - 2049 u) times the magnitudes
+    mag = np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T + np.abs(b.astype(np.float64))
+    g = 2049 * 2.0 ** -24 / (1 - 2049 * 2.0 ** -24)
+    assert np.allclose(beta, g * mag, rtol=1e-15, atol=0)
+
+
+def test_router_bound_covers_three_part_split():
+    """The logits evaluated as 3 H exact products of x with the bf16 parts of each
+    fp32 weight (hi, mid, lo by truncation), summed in fp32, stay within the
+    three-part bound; the parts are exact (hi + mid + lo == w)."""
+    x, w, b = _router_case()
+    trunc = lambda a: (np.asarray(a, np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32)
+    hi = trunc(w)
+    mid = trunc((w - hi).astype(np.float32))
+    lo = ((w - hi).astype(np.float32) - mid).astype(np.float32)
+    assert np.array_equal(hi.astype(np.float64) + mid + lo, w.astype(np.float64))
+    exact = mo.router_logits(x, w, b)
+    beta3 = mo.router_error_bound(x, w, b, parts=3)
+    acc = np.zeros((3, 16), np.float32)
+    for part in (lo, mid, hi):
+        for i in range(2048):
+            acc = (acc + x[:, i:i + 1] * part[None, :, i]).astype(np.float32)
+    acc = (acc + b).astype(np.float32)
+    assert np.all(np.abs(acc.astype(np.float64) - exact) <= beta3)
+    assert np.all(beta3 > mo.router_error_bound(x, w, b))
 
 
 def test_certify_ids_rules():
