@@ -5,19 +5,25 @@ SwiGLU with in-register dequant, shared expert, combine) for one decode token
 through a 512-expert top-10 + 1 shared layer (H 2048, I 768, 4-bit group-32
 weights, bf16 activations), with the inputs resident in HBM.  Consecutive
 steps rotate over 16 distinct copies of the layer's weights (21.8 GB) so the
-experts stream from HBM and not from the 256 MB last-level cache.
+experts stream from HBM and not from the 256 MB last-level cache.  The K timed
+steps are replayed from captured HIP graphs (16 steps per graph); the same
+steps launched directly are reported beside them.
 
 Prints one JSON line (rank 0, N = 1):
   value        decode tokens/s (whole job)
-  roofline     HBM roofline of the dominant kernel (expert gate/up + SwiGLU),
-               algorithmic bytes per launch / HIP-event time per launch
-  cpu_baseline the CPU oracle on a bounded sample of the same workload
-plus extra fields: expert-weight GB/s of the whole layer, the same decode steps
-and gate/up launches replayed from captured HIP graphs, prefill tokens/s, the
-5-token verify batch and one decode step through the 48-layer 2-bit stack at
-batch 1 and 8 (expert planes filled on the device).
+  roofline     HBM roofline of the decode step: algorithmic bytes per step
+               (router, the selected and shared experts, x and y) / time per step
+  cpu_baseline the CPU oracle on a bounded sample of the same workload (all
+               host cores and one thread)
+plus extra fields: expert-weight GB/s, the directly launched steps (and the
+median of 5 more repetitions), prefill tokens/s and MFMA fraction, the 5-token
+verify batch, a batch sweep T = 8 .. 256 in each weight format, and one decode
+step through the 48-layer 2-bit stack at batch 1 and 8 (expert planes filled
+on the device), each with its distinct experts, algorithmic bytes and fraction
+of 8 TB/s.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-prefill] [--no-graph] [--no-stack]
+                    [--no-sweep]
 """
 from __future__ import annotations
 
@@ -32,14 +38,14 @@ import numpy as np
 
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per launch of the roofline kernel (k_gateup1, one token, 10 experts +
-# shared) from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) over this
-# script, each scaled by what the counter reads for a 256 MiB device copy
-# (FETCH_SIZE x 1.99981, WRITE_SIZE x 1.0).  Valid for the kernel sources whose
-# fingerprint is stored; reported as null once they change.
-TRAFFIC_SOURCES = ("expert_gemv.hip", "gemv_one.h", "gemv_tile.h", "moe_device.h", "topk.h", "moe_internal.h")
-MEASURED_TRAFFIC = {"bytes_per_launch": 19604844,
-                    "sources_sha256": "2a1801e1b42238b9c43c6588bae4d8f5b90d526225c6d301b0c8c754ac4e5bcf"}
+# HBM bytes of one decode step (the sum over its three kernels, one token, 10
+# experts + shared) from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE)
+# over this script, each scaled by what the counter reads for a device copy of
+# known size run in the same pass (--copy-calib-mib).  Valid for the kernel
+# sources whose fingerprint is stored; reported as null once they change.
+TRAFFIC_SOURCES = ("router.hip", "expert_gemv.hip", "gemv_one.h", "gemv_tile.h", "moe_device.h", "topk.h",
+                   "moe_internal.h", "moe_abi.cpp")
+MEASURED_TRAFFIC = {"bytes_per_step": None, "sources_sha256": ""}
 
 
 def kernel_sources_sha256() -> str:
@@ -69,6 +75,7 @@ def main():
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the verify batch (5 tokens, 2-bit) and the 48-layer 2-bit stack figures")
     ap.add_argument("--stack-steps", type=int, default=20)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the batch sweep T = 8 .. 256")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra timing of the same steps replayed from captured HIP graphs")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -140,98 +147,75 @@ def main():
         bound_steps[(args.warmup + i) % period]()
     end.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
-    tok_s = 1e3 / ms_per_step
-    log(f"decode: {ms_per_step * 1e3:.2f} us/step, {tok_s:.0f} tok/s")
+    direct_us = start.elapsed_time(end) * 1e3 / args.steps
+    log(f"decode, direct launches: {direct_us:.2f} us/step")
 
-    # extra: the same steps replayed from captured HIP graphs (a serving loop's
-    # way of launching a step), args.copies steps per graph, 8 graphs over
-    # different tokens, cycled
+    # the timed steps replayed from captured HIP graphs (a serving loop's way of
+    # launching a step): graphs of up to 16 consecutive steps, the K timed
+    # steps covered exactly, the same (copy, token) sequence as above
     graph_us = None
+    decode_launch = "direct"
+    ms_per_step = direct_us * 1e-3
     if not args.no_graph:
-        g_steps, n_graphs = args.copies, 8
         cap = torch.cuda.Stream()
+        g_len = 16
 
-        def capture(first):
+        def capture(first, n):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
-                for i in range(g_steps):
+                for i in range(n):
                     step(first + i, torch.cuda.current_stream())
             return g
 
-        graphs = [capture(j * g_steps) for j in range(n_graphs)]
+        graphs = [capture(args.warmup + i, min(g_len, args.steps - i)) for i in range(0, args.steps, g_len)]
         for g in graphs:  # warm replays
             g.replay()
         torch.cuda.synchronize()
-        reps = max(1, args.steps // g_steps)
         start.record(stream)
-        for r in range(reps):
-            graphs[r % n_graphs].replay()
+        for g in graphs:
+            g.replay()
         end.record(stream)
         torch.cuda.synchronize()
-        graph_us = start.elapsed_time(end) * 1e3 / (reps * g_steps)
+        graph_us = start.elapsed_time(end) * 1e3 / args.steps
         log(f"decode, HIP graph replay: {graph_us:.2f} us/step")
+        decode_launch = "HIP graph replay (graphs of 16 steps)"
+        ms_per_step = graph_us * 1e-3
+    tok_s = 1e3 / ms_per_step
+    log(f"decode: {ms_per_step * 1e3:.2f} us/step, {tok_s:.0f} tok/s ({decode_launch})")
 
     # routing of each copy for its first timed token: distinct experts per step
     wts = torch.empty((1, K), dtype=torch.float32, device=dev)
-    idss = [torch.empty((1, K), dtype=torch.int32, device=dev) for _ in range(args.copies)]
-    offs = [torch.empty(E + 1, dtype=torch.int32, device=dev) for _ in range(args.copies)]
-    sps = [torch.empty(K, dtype=torch.int32, device=dev) for _ in range(args.copies)]
-    pp = torch.empty(K, dtype=torch.int32, device=dev)
+    ids1 = torch.empty((1, K), dtype=torch.int32, device=dev)
     distinct = []
     for c in range(args.copies):
-        api.moe_router_topk(layers[c], xs[c:c + 1], 1, idss[c], wts, ws=ws)
-        api.moe_permute(layers[c], idss[c], 1, offs[c], sps[c], pp, ws)
-        distinct.append(len(set(idss[c].cpu().numpy().reshape(-1).tolist())))
+        api.moe_router_topk(layers[c], xs[c:c + 1], 1, ids1, wts, ws=ws)
+        distinct.append(len(set(ids1.cpu().numpy().reshape(-1).tolist())))
     u_mean = float(np.mean(distinct))
 
-    # dominant kernel: expert gate/up + SwiGLU (one kernel per call), timed
-    # with HIP events on the stream it runs on, launches back to back (bound
-    # calls, as for the steps above)
-    h = torch.empty((K, I), dtype=torch.bfloat16, device=dev)
-    hs = torch.empty((1, I), dtype=torch.bfloat16, device=dev)
-    for r in range(50):
-        c = r % args.copies
-        api.moe_expert_gate_up_q(layers[c], xs[c:c + 1], 1, idss[c], offs[c], sps[c], h, hs, stream=stream)
-    torch.cuda.synchronize()
-    bound_gu = [api.bind_expert_gate_up_q(layers[c], xs[c:c + 1], 1, idss[c], offs[c], sps[c], h, hs, stream=stream)
-                for c in range(args.copies)]
-    start.record(stream)
-    for r in range(args.kernel_reps):
-        bound_gu[r % args.copies]()
-    end.record(stream)
-    torch.cuda.synchronize()
-    k_us = start.elapsed_time(end) * 1e3 / args.kernel_reps
-    # the same launches replayed from a captured graph
-    k_graph_us = None
-    gg = torch.cuda.CUDAGraph() if not args.no_graph else None
-    if gg is not None:
-        with torch.cuda.graph(gg, stream=torch.cuda.Stream()):
-            for c in range(args.copies):
-                api.moe_expert_gate_up_q(layers[c], xs[c:c + 1], 1, idss[c], offs[c], sps[c], h, hs)
-        gg.replay()
-        torch.cuda.synchronize()
-        reps = max(1, args.kernel_reps // args.copies)
+    # median of 5 more repetitions of the timed loop (directly launched steps)
+    reps5 = []
+    for r in range(5):
         start.record(stream)
-        for r in range(reps):
-            gg.replay()
+        for i in range(max(args.steps, 200)):
+            bound_steps[(r * 997 + i) % period]()
         end.record(stream)
         torch.cuda.synchronize()
-        k_graph_us = start.elapsed_time(end) * 1e3 / (reps * args.copies)
-    gu_bytes_unit = 2 * workload.matrix_bytes(spec.qfmt, I, H)       # gate + up of one expert
-    gu_bytes = (u_mean + 1) * gu_bytes_unit + (u_mean + 1) * H * 2 + (K + 1) * I * 2  # + x reads, h writes
-    achieved = gu_bytes / (k_us * 1e-6) / 1e9
-    log(f"gate/up kernel: {k_us:.2f} us/launch, {achieved:.0f} GB/s")
+        reps5.append(start.elapsed_time(end) * 1e3 / max(args.steps, 200))
+    log(f"decode, 5 more repetitions of {max(args.steps, 200)} steps: " + ", ".join(f"{v:.2f}" for v in reps5) + " us")
 
     exp_bytes = workload.expert_weight_bytes(spec.qfmt, H, I, int(round(u_mean)), spec.n_shared)
     layer_bytes = workload.spec_layer_bytes(spec, int(round(u_mean)), tokens=1)
+    achieved = layer_bytes / (ms_per_step * 1e-3) / 1e9
     extra = {
         "expert_weight_GBps": exp_bytes / (ms_per_step * 1e-3) / 1e9,
         "expert_weight_frac_of_8TBps": exp_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "layer_algorithmic_GBps": layer_bytes / (ms_per_step * 1e-3) / 1e9,
+        "layer_algorithmic_GBps": achieved,
         "layer_algorithmic_bytes": layer_bytes,
+        "decode_launch": decode_launch,
+        "decode_direct_launch_us_per_step": direct_us,
         "decode_graph_replay_us_per_step": graph_us,
-        "gateup_graph_replay_us_per_launch": k_graph_us,
+        "decode_direct_us_per_step_median5": float(np.median(reps5)),
+        "decode_direct_us_per_step_reps5": reps5,
         "distinct_experts_per_token": u_mean,
         "weight_copies": args.copies,
     }
@@ -256,7 +240,7 @@ def main():
         log(f"prefill: {pms:.3f} ms/layer, {extra['prefill_tok_s']:.0f} tok/s")
 
     if not args.no_stack:
-        extra.update(verify_and_stack(args, dev))
+        extra.update(verify_and_stack(args, dev, q4_layers=layers))
 
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
@@ -268,7 +252,7 @@ def main():
         del src, dst
         log(f"copy calibration: 4 copies of {args.copy_calib_mib} MiB")
 
-    traffic = (MEASURED_TRAFFIC["bytes_per_launch"]
+    traffic = (MEASURED_TRAFFIC["bytes_per_step"]
                if MEASURED_TRAFFIC["sources_sha256"] == kernel_sources_sha256() else None)
 
     cpu = None
@@ -286,18 +270,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32",  # fp32 arithmetic on bf16 activations and 4-bit codes
         "data": "synthetic",
         "config": {
             "workload": "decode: 1 token/step through one routed MoE FFN layer, hidden 2048, 512 experts, "
                         "top-10 + 1 shared, intermediate 768, 4-bit sym group-32 fp16-scale weights, bf16 activations, "
-                        "fp32 router with Zipf(1.1) bias; 16 rotating weight copies",
+                        "fp32 router with Zipf(1.1) bias; 16 rotating weight copies; steps launched as "
+                        + decode_launch,
             "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)",
         },
         "roofline": {
-            "bound": "hbm", "kernel": "expert gate/up + SwiGLU, one token (k_gateup1)",
+            "bound": "hbm",
+            "kernel": "the whole decode layer step (k_router_logits, k_fused_gateup1, k_fused_down1): "
+                      "algorithmic bytes per step / time per step",
             "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-            "traffic": traffic, "us_per_launch": k_us, "algorithmic_bytes_per_launch": gu_bytes,
+            "traffic": traffic, "us_per_launch": ms_per_step * 1e3, "algorithmic_bytes_per_launch": layer_bytes,
         },
         "cpu_baseline": cpu,
         "extra": extra,
@@ -305,42 +292,84 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def verify_and_stack(args, dev):
-    """Extra figures on the 2-bit format, with expert planes filled on the device:
-    the speculative-verify batch (5 tokens through one layer, 16 layer copies
-    rotating) and one decode step through the 48-layer stack at batch 1 and 8."""
+def _distinct(layer, x, T, ws, dev):
+    """Distinct experts selected by the T tokens of one step (routing on the device)."""
+    import torch
+
+    from sparse_moe_router_amd import api
+    ids = torch.empty((T, layer.top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, layer.top_k), dtype=torch.float32, device=dev)
+    api.moe_router_topk(layer, x, T, ids, w, ws=ws)
+    return len(np.unique(ids.cpu().numpy()))
+
+
+def _time_steps(fn, n, stream):
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(n):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / n
+
+
+def batch_figures(spec, layers, T, xpool, ws, y, stream, dev, n_steps, prefix):
+    """T tokens per step through rotating layer copies: us/step, tokens/s, the mean
+    distinct experts U, the algorithmic bytes per step and their fraction of 8 TB/s."""
+    from sparse_moe_router_amd import api, workload
+    n_win = xpool.shape[0] // T
+    copies = len(layers)
+    u = [_distinct(layers[i % copies], xpool[(i % n_win) * T:(i % n_win + 1) * T], T, ws, dev)
+         for i in range(min(copies * n_win, 32))]
+    bound = [api.bind_layer_forward(layers[i % copies], xpool[(i % n_win) * T:(i % n_win + 1) * T], T, y, ws=ws,
+                                    stream=stream) for i in range(min(copies * n_win, 64))]
+    for i in range(min(len(bound), 20)):
+        bound[i]()
+    us = _time_steps(lambda i: bound[i % len(bound)](), n_steps, stream)
+    u_mean = float(np.mean(u))
+    b = float(np.mean([workload.spec_layer_bytes(spec, v, tokens=T) for v in u]))
+    return {f"{prefix}_us_per_step": us, f"{prefix}_tok_s": T / (us * 1e-6), f"{prefix}_distinct_experts": u_mean,
+            f"{prefix}_algorithmic_bytes": b, f"{prefix}_frac_of_8TBps": b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+
+
+def verify_and_stack(args, dev, q4_layers=None):
+    """Extra figures with expert planes filled on the device (2-bit format unless
+    stated): the speculative-verify batch (5 tokens through one layer, 16 layer
+    copies rotating), the batch sweep T = 8 .. 256 (2-bit, and 4-bit on the
+    decode copies), and one decode step through the 48-layer stack at batch 1
+    and 8, each with its distinct experts, algorithmic bytes and fraction of
+    8 TB/s."""
     import torch
 
     import synth
     from sparse_moe_router_amd import api, workload
     from synth import torch_io
     out = {}
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
 
     vs = synth.SPECS["verify"]
     vlayers = [api.Layer(**torch_io.device_filled_kwargs(vs, c, dev)) for c in range(args.copies)]
-    xv = torch_io.x_tensor(synth.gen_x(vs, seed=0, tokens=64 * vs.tokens).storage, vs.act, dev)
-    ws = api.workspace(vlayers[0], vs.tokens, dev)
-    yv = torch.empty((vs.tokens, vs.hidden), dtype=torch.float32, device=dev)
-
-    def vstep(i):
-        t0 = (i % 64) * vs.tokens
-        api.moe_layer_forward(vlayers[i % args.copies], xv[t0:t0 + vs.tokens], vs.tokens, yv, ws=ws, stream=stream)
-
-    for i in range(50):
-        vstep(i)
-    torch.cuda.synchronize()
-    n = max(200, args.steps // 4)
-    start.record(stream)
-    for i in range(n):
-        vstep(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    us = start.elapsed_time(end) * 1e3 / n
-    out["verify_T5_q2_us_per_step"] = us
-    out["verify_T5_q2_tok_s"] = vs.tokens / (us * 1e-6)
-    log(f"verify (T=5, 2-bit): {us:.2f} us/step")
+    xv = torch_io.x_tensor(synth.gen_x(vs, seed=0, tokens=4096).storage, vs.act, dev)
+    ws = api.workspace(vlayers[0], 256, dev)
+    yv = torch.empty((256, vs.hidden), dtype=torch.float32, device=dev)
+    f = batch_figures(vs, vlayers, vs.tokens, xv, ws, yv, stream, dev, max(200, args.steps // 4), "verify_T5_q2")
+    out.update(f)
+    log(f"verify (T=5, 2-bit): {f['verify_T5_q2_us_per_step']:.2f} us/step, U = "
+        f"{f['verify_T5_q2_distinct_experts']:.1f}, {100 * f['verify_T5_q2_frac_of_8TBps']:.1f} % of 8 TB/s")
+    if not args.no_sweep:
+        sweep = {}
+        for fmt, ls, sp in (("q2", vlayers, vs), ("q4", q4_layers, synth.SPECS["decode"])):
+            if ls is None:
+                continue
+            xq = xv if fmt == "q2" else torch_io.x_tensor(synth.gen_x(sp, seed=1, tokens=4096).storage, sp.act, dev)
+            for T in (8, 16, 32, 64, 128, 256):
+                g = batch_figures(sp, ls, T, xq, ws, yv, stream, dev, max(20, 1600 // T), f"T{T}")
+                sweep[f"{fmt}_T{T}"] = {k.split("_", 1)[1]: v for k, v in g.items()}
+                log(f"batch sweep {fmt} T={T}: {g[f'T{T}_us_per_step']:.1f} us/step, "
+                    f"{g[f'T{T}_tok_s']:.0f} tok/s, U = {g[f'T{T}_distinct_experts']:.1f}, "
+                    f"{100 * g[f'T{T}_frac_of_8TBps']:.1f} % of 8 TB/s")
+        out["batch_sweep"] = sweep
     del vlayers, ws
     torch.cuda.empty_cache()
 
@@ -354,45 +383,73 @@ def verify_and_stack(args, dev):
         spec = synth.SPECS["stack_t1" if T == 1 else "stack_t8"]
         ws = api.workspace(stack[0], T, dev)
         base = torch_io.x_tensor(synth.gen_x(spec, seed=0, tokens=T).storage, spec.act, dev)
+        # the distinct experts of every layer on this input (the residual stream
+        # through the layers, as the stack computes it)
+        cur = base.clone()
+        u = []
+        for L in stack:
+            u.append(_distinct(L, cur, T, ws, dev))
+            api.moe_layer_forward(L, cur, T, torch.empty((T, spec.hidden), dtype=torch.float32, device=dev),
+                                  x_next=cur, ws=ws, stream=stream)
+        torch.cuda.synchronize()
         xs = [base.clone() for _ in range(args.stack_steps + 2)]  # each step starts from the same x
         for k in range(2):
             api.moe_stack_forward(stack, xs[k], T, ws=ws, stream=stream)
         torch.cuda.synchronize()
-        start.record(stream)
-        for k in range(args.stack_steps):
-            api.moe_stack_forward(stack, xs[2 + k], T, ws=ws, stream=stream)
-        end.record(stream)
-        torch.cuda.synchronize()
-        us = start.elapsed_time(end) * 1e3 / args.stack_steps
+        us = _time_steps(lambda k: api.moe_stack_forward(stack, xs[2 + k], T, ws=ws, stream=stream),
+                         args.stack_steps, stream)
+        b = float(sum(workload.spec_layer_bytes(ss, v, tokens=T) for v in u))
         out[f"stack48_q2_T{T}_us_per_step"] = us
         out[f"stack48_q2_T{T}_tok_s"] = T / (us * 1e-6)
-        if T == 1:
-            b = ss.n_layers * workload.spec_layer_bytes(ss, ss.top_k, tokens=1)
-            out["stack48_q2_T1_algorithmic_GBps"] = b / (us * 1e-6) / 1e9
-        log(f"48-layer stack, T={T}: {us:.1f} us/step ({T / (us * 1e-6):.0f} tok/s)")
+        out[f"stack48_q2_T{T}_distinct_experts_per_layer"] = float(np.mean(u))
+        out[f"stack48_q2_T{T}_algorithmic_bytes"] = b
+        out[f"stack48_q2_T{T}_frac_of_8TBps"] = b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS
+        log(f"48-layer stack, T={T}: {us:.1f} us/step ({T / (us * 1e-6):.0f} tok/s), U per layer "
+            f"{np.mean(u):.1f}, {100 * out[f'stack48_q2_T{T}_frac_of_8TBps']:.1f} % of 8 TB/s")
         del ws, xs
     return out
 
 
+def _host_cpu():
+    model = None
+    try:
+        import subprocess
+        for line in subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except Exception:  # pragma: no cover
+        pass
+    return model
+
+
 def cpu_baseline(spec, ld):
-    """The oracle (float64 NumPy) on decode tokens of the same layer, for about 12 s (at most 256 tokens)."""
+    """The oracle (float64 NumPy) on decode tokens of the same layer: with the BLAS
+    threads at their default (all host cores) and at 1 thread, each the median
+    of 3 runs of about 4 s (at most 96 tokens each)."""
     import synth
     from oracle import moe_oracle as mo
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    x = synth.gen_x(spec, seed=0, tokens=256).values
-    t0 = time.time()
-    n = 0
-    while n < 256 and (time.time() - t0 < 12.0 or n < 2):
-        mo.layer_forward(ld, x[n:n + 1], keep_expert_out=False)
-        n += 1
-    dt = time.time() - t0
-    log(f"cpu oracle: {n} tokens in {dt:.1f}s")
-    return {"value": n / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} decode tokens (T=1 each) through the same 512-expert 4-bit layer, float64 NumPy"}
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    x = synth.gen_x(spec, seed=0, tokens=96).values
+
+    def run():
+        t0 = time.time()
+        n = 0
+        while n < 96 and (time.time() - t0 < 4.0 or n < 2):
+            mo.layer_forward(ld, x[n:n + 1], keep_expert_out=False)
+            n += 1
+        return n / (time.time() - t0), n
+
+    all_cores = [run() for _ in range(3)]
+    with threadpool_limits(limits=1):
+        one = [run() for _ in range(3)]
+    v_all = float(np.median([r for r, _ in all_cores]))
+    v_one = float(np.median([r for r, _ in one]))
+    log(f"cpu oracle: {v_all:.2f} tok/s on {threads} BLAS threads, {v_one:.2f} tok/s on 1 thread")
+    return {"value": v_all, "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": "decode tokens (T=1 each) through the same 512-expert 4-bit layer, float64 NumPy; median of 3 "
+                      f"runs of about 4 s ({', '.join(str(n) for _, n in all_cores)} tokens)",
+            "single_thread_value": v_one, "os_cpu_count": os.cpu_count(), "host_cpu": _host_cpu()}
 
 
 if __name__ == "__main__":

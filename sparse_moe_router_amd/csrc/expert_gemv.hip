@@ -32,10 +32,12 @@ __device__ __forceinline__ bool next_routed(const FfnArgs& a, int ny, int* pos, 
     const int pp = j > 0 ? a.sorted_pairs[j - 1] : pj;
     const int e = a.ids[pj];
     if (j == 0 || a.ids[pp] != e) {
+      const int cnt = a.offsets[e + 1] - j;
+      if (on_mfma(a, cnt)) continue;  // the grouped GEMM takes this expert
       w->expert = e;
       w->lo = j;
       w->pair0 = pj;
-      w->n = a.offsets[e + 1] - j;
+      w->n = cnt;
       *pos += ny;
       return true;
     }
@@ -129,6 +131,7 @@ template <int QF, int ACT, int NT, int GPL, int RPW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd(ACT, NT, GPL)))) void k_gateup(
     FfnArgs a, int ny, int lpr_log2) {
   const bool shared = (int)blockIdx.y == ny;  // the extra last row of blocks
+  if (shared && on_mfma(a, a.T)) return;
   int pos = blockIdx.y;
   Work wk;
   if (shared) { wk.expert = -1; wk.lo = 0; wk.n = a.T; wk.pair0 = 0; }
@@ -216,6 +219,7 @@ template <int QF, int ACT, int NT, int GPL, int RPW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_simd(ACT, NT, GPL)))) void k_down(FfnArgs a, int ny,
                                                                                     int lpr_log2) {
   const bool shared = (int)blockIdx.y == ny;
+  if (shared && on_mfma(a, a.T)) return;
   int pos = blockIdx.y;
   Work wk;
   if (shared) { wk.expert = -1; wk.lo = 0; wk.n = a.T; }
@@ -341,9 +345,14 @@ static hipError_t gateup1_q(const FfnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
-  if (a.T == 0) return hipSuccess;
-  if (mfma_ok(a)) return launch_mfma_gateup(a, s);
+hipError_t launch_gateup(const FfnArgs& args, hipStream_t s) {
+  if (args.T == 0) return hipSuccess;
+  FfnArgs a = args;
+  a.mfma_min = mfma_split(a);
+  if (a.mfma_min > 0) {
+    const hipError_t e = launch_mfma_gateup(a, s);
+    if (e != hipSuccess || a.mfma_min == 1) return e;
+  }
   if (gateup1_ok(a))
     return a.qfmt == MOE_Q4_SYM_G32 ? gateup1_q<MOE_Q4_SYM_G32>(a, s) : gateup1_q<MOE_Q2_ASYM_G32>(a, s);
   if (gateup_sb_ok(a)) return launch_gateup_sb(a, s);
@@ -353,9 +362,14 @@ hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
 template <int QF> static hipError_t down1_q(const FfnArgs& a, hipStream_t s);
 bool down1_ok(const FfnArgs& a);
 
-hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
-  if (a.T == 0) return hipSuccess;
-  if (mfma_ok(a)) return launch_mfma_down(a, s);
+hipError_t launch_down(const FfnArgs& args, hipStream_t s) {
+  if (args.T == 0) return hipSuccess;
+  FfnArgs a = args;
+  a.mfma_min = mfma_split(a);
+  if (a.mfma_min > 0) {
+    const hipError_t e = launch_mfma_down(a, s);
+    if (e != hipSuccess || a.mfma_min == 1) return e;
+  }
   if (down1_ok(a)) return a.qfmt == MOE_Q4_SYM_G32 ? down1_q<MOE_Q4_SYM_G32>(a, s) : down1_q<MOE_Q2_ASYM_G32>(a, s);
   if (down_sb_ok(a)) return launch_down_sb(a, s);
   return a.qfmt == MOE_Q4_SYM_G32 ? dispatch_act<MOE_Q4_SYM_G32>(a, false, s) : dispatch_act<MOE_Q2_ASYM_G32>(a, false, s);

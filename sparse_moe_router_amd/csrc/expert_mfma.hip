@@ -63,8 +63,8 @@ __device__ __forceinline__ void unpack_b(uint32_t w, uint32_t (&b)[4]) {
   }
 }
 
-// Work tiles: ceil(n_e / 64) per routed expert in expert order, then
-// ceil(T / 64) for the shared expert.  Every wave of a block derives its tile
+// Work tiles: ceil(n_e / 64) per routed expert with n_e >= mfma_min tokens,
+// in expert order, then ceil(T / 64) for the shared expert (if T >= mfma_min).  Every wave of a block derives its tile
 // from the expert offsets (a wave-wide scan of the per-expert tile counts), so
 // the tiling needs no list in memory.  Returns false past the last tile.
 __device__ __forceinline__ bool find_tile(const FfnArgs& a, bool with_shared, int t, int& expert, int& m0) {
@@ -79,7 +79,10 @@ __device__ __forceinline__ bool find_tile(const FfnArgs& a, bool with_shared, in
 #pragma unroll
     for (int i = 0; i <= kPer; ++i) v[i] = a.offsets[min(e0 + base + i, e_end)];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) c[i] = (v[i + 1] - v[i] + kBM - 1) / kBM;
+    for (int i = 0; i < kPer; ++i) {
+      const int n = v[i + 1] - v[i];
+      c[i] = n >= a.mfma_min ? (n + kBM - 1) / kBM : 0;  // experts with fewer tokens: the GEMV kernels
+    }
   };
   int c[kPer];
   int cnt = 0;
@@ -98,7 +101,7 @@ __device__ __forceinline__ bool find_tile(const FfnArgs& a, bool with_shared, in
   if (t >= routed) {
     expert = -1;
     m0 = (t - routed) * kBM;
-    return with_shared && m0 < a.T;
+    return with_shared && a.T >= a.mfma_min && m0 < a.T;
   }
   const int owner = __ffsll((unsigned long long)__ballot(incl > t)) - 1;
   int local = t - (incl - cnt), e_hit = 0, m_hit = 0;
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int n_rows = shared ? a.T : a.offsets[expert + 1] - lo;  // tokens of this expert
   const int kdim = NMAT == 2 ? a.H : a.I;   // reduction length
   const int rows = NMAT == 2 ? a.I : a.H;   // output rows per matrix
-  const int G = kdim / kGroup;  // a multiple of kChunkG (checked by mfma_ok)
+  const int G = kdim / kGroup;  // a multiple of kChunkG (checked by mfma_capable)
   const int nchunks = G / kChunkG;
 
   __shared__ __align__(16) uint32_t s_a[2][kBM * kRowWords];
@@ -447,10 +450,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
 }
 
-// Upper bound of the tile count: sum_e ceil(n_e / 64) <= T K / 64 + (experts hit).
+// Upper bound of the tile count: sum over the experts with n_e >= mfma_min of
+// ceil(n_e / 64) <= T K / 64 + min(E, T K / mfma_min), plus the shared tiles.
 static int tile_capacity(const FfnArgs& a, bool with_shared) {
   const int64_t pairs = (int64_t)a.T * a.K;
-  return (int)(pairs / kBM + (pairs < a.E ? pairs : a.E) + (with_shared ? (a.T + kBM - 1) / kBM : 0));
+  const int64_t hot = pairs / (a.mfma_min > 1 ? a.mfma_min : 1);
+  return (int)(pairs / kBM + (hot < a.E ? hot : a.E) +
+               (with_shared && a.T >= a.mfma_min ? (a.T + kBM - 1) / kBM : 0));
 }
 
 // Matrix-core path: bf16 activations (the A operand is the activation
@@ -459,11 +465,25 @@ static int tile_capacity(const FfnArgs& a, bool with_shared) {
 static bool al8(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 7) == 0; }
 static bool qm_al8(const QMat& q) { return al8(q.scales) && al8(q.mins); }
 
-bool mfma_ok(const FfnArgs& a) {
+static bool mfma_capable(const FfnArgs& a) {
   const int chunk = kGroup * kChunkG;
-  return a.act == MOE_ACT_BF16 && (int64_t)a.T * a.K >= 8 * (int64_t)a.E && a.H % chunk == 0 && a.I % chunk == 0 &&
-         qm_al8(a.gate) && qm_al8(a.up) && qm_al8(a.down) && (!a.n_shared || (qm_al8(a.sgate) && qm_al8(a.sup) &&
-                                                                               qm_al8(a.sdown)));
+  return a.act == MOE_ACT_BF16 && a.H % chunk == 0 && a.I % chunk == 0 && qm_al8(a.gate) && qm_al8(a.up) &&
+         qm_al8(a.down) && (!a.n_shared || (qm_al8(a.sgate) && qm_al8(a.sup) && qm_al8(a.sdown)));
+}
+
+// The expert split for T tokens (FfnArgs::mfma_min): every expert on the
+// grouped GEMM from 8 tokens per expert on average; below that, past the
+// small-batch pair count, only the experts with at least kHotTokens tokens
+// (under the router's skew a few experts take most of the tokens: a GEMV
+// block row would walk them a few tokens at a time); none for fewer pairs.
+constexpr int kHotTokens = 8;
+constexpr int kSplitMinPairs = 256;
+int mfma_split(const FfnArgs& a) {
+  if (!mfma_capable(a)) return 0;
+  const int64_t pairs = (int64_t)a.T * a.K;
+  if (pairs >= 8 * (int64_t)a.E) return 1;
+  if (pairs > kSplitMinPairs) return 1;
+  return 0;
 }
 
 hipError_t launch_mfma_gateup(const FfnArgs& a, hipStream_t s) {

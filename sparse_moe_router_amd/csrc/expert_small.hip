@@ -25,14 +25,14 @@ constexpr int kSbMaxPairs = 256;  // T K of the small-batch path (one block row 
 __device__ __forceinline__ bool sb_work(const FfnArgs& a, int ny, int y, int* expert, int* lo, int* n) {
   if (y == ny) {
     *expert = -1; *lo = 0; *n = a.T;
-    return true;
+    return !on_mfma(a, a.T);
   }
   const int p = a.sorted_pairs[y];
   const int pp = y > 0 ? a.sorted_pairs[y - 1] : p;
   const int e = a.ids[p];
   if (y > 0 && a.ids[pp] == e) return false;
   *expert = e; *lo = y; *n = a.offsets[e + 1] - y;
-  return true;
+  return !on_mfma(a, *n);  // the grouped GEMM takes an expert with many tokens
 }
 
 // token of the expert's jj-th sorted position

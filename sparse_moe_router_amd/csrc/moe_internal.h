@@ -61,7 +61,14 @@ struct FfnArgs {
   void* hs;                    // [T][I] act, shared
   float* o;                    // [T*K][H] fp32, sorted order
   float* so;                   // [T][H] fp32, shared (null: shared expert skipped)
+  // Split of the experts between the kernel families: experts with at least
+  // mfma_min tokens (and the shared expert when T >= mfma_min) run on the
+  // matrix-core grouped GEMM, the others on the GEMV kernels.  0: no split
+  // (the GEMV kernels take every expert; the grouped GEMM is not launched).
+  int mfma_min;
 };
+// the GEMV kernels skip an expert with n tokens that the grouped GEMM takes
+__host__ __device__ inline bool on_mfma(const FfnArgs& a, int n) { return a.mfma_min > 0 && n >= a.mfma_min; }
 hipError_t launch_gateup(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 // small batches (1 < T, T K <= 256, bf16; H <= 2048 for gate/up, I <= 1024 for
@@ -71,9 +78,11 @@ bool gateup_sb_ok(const FfnArgs& a);
 bool down_sb_ok(const FfnArgs& a);
 hipError_t launch_gateup_sb(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down_sb(const FfnArgs& a, hipStream_t s);
-// matrix-core grouped GEMMs for many tokens per expert (launch_gateup and
-// launch_down take this path themselves when mfma_ok holds)
-bool mfma_ok(const FfnArgs& a);
+// matrix-core grouped GEMMs for many tokens per expert: launch_gateup and
+// launch_down set FfnArgs::mfma_min = mfma_split(a) and run the grouped GEMM
+// for the experts it assigns (all of them when it returns 1), then the GEMV
+// kernels for the rest
+int mfma_split(const FfnArgs& a);
 hipError_t launch_mfma_gateup(const FfnArgs& a, hipStream_t s);
 hipError_t launch_mfma_down(const FfnArgs& a, hipStream_t s);
 

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 // Block: 64 tokens x 64 experts, 4 waves; wave w owns experts n0 + 16 w ..
 // + 15 and all 64 tokens (4 MFMA tiles of 16 x 16); the x tile is staged
 // through LDS in 128-k chunks (double buffered), shared by the 4 waves.
-constexpr int kRouterMfmaMinTokens = 32;
+constexpr int kRouterMfmaMinTokens = 128;
 constexpr int kRM = 64, kRN = 64, kRKC = 128;
 constexpr int kRRow = kRKC + 8;  // bf16 per LDS row (+8: conflict-free 16-byte reads)
 

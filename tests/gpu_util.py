@@ -70,12 +70,12 @@ def run_forward(L: api.Layer, x: torch.Tensor, T: int, x_next=False):
 
 # bf16 activations and at least this many tokens: the library evaluates the
 # logits on the matrix cores with each fp32 weight split into three bf16 parts
-ROUTER_MFMA_MIN_TOKENS = 32
+ROUTER_MFMA_MIN_TOKENS = 128
 
 
 def router_parts(spec, T):
     """Parts per weight of the library's logit evaluation for a call of T tokens:
-    3 on the matrix-core path (bf16 x, T >= 32), else 1 (an fp32 dot product)."""
+    3 on the matrix-core path (bf16 x, T >= 128), else 1 (an fp32 dot product)."""
     return 3 if spec.act == synth.ACT_BF16 and T >= ROUTER_MFMA_MIN_TOKENS else 1
 
 
@@ -197,3 +197,19 @@ def check_y_teacher_forced(ld, xv, gpu, tol=2e-3):
         assert rs <= tol, f"teacher-forced shared_out max|do| = {rs:.3e} x RMS exceeds {tol}"
     direct, _ = rel_err(gpu["y"], ref["y"])
     return r, direct, flips
+
+
+def pairs_direct(ld, xv, gpu, tol=2e-3, bar=False):
+    """The routed expert outputs (one row per pair, sorted order) and the shared
+    expert's output against the oracle evaluated with the GPU's ids and its own
+    rounding of h (no teacher forcing): max|do| / RMS(o) over all pairs.  With
+    ``bar`` both must be within tol.  Returns (routed, shared) ratios."""
+    ref = mo.layer_forward(ld, xv, ids=gpu["ids"])
+    ro, _ = rel_err(gpu["expert_out"], ref["expert_out"])
+    rs = 0.0
+    if gpu.get("shared_out") is not None and ld.shared.n:
+        rs, _ = rel_err(gpu["shared_out"], ref["shared_out"])
+    if bar:
+        assert ro <= tol, f"expert_out max|do| = {ro:.3e} x RMS exceeds {tol}"
+        assert rs <= tol, f"shared_out max|do| = {rs:.3e} x RMS exceeds {tol}"
+    return ro, rs
