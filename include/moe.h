@@ -31,8 +31,10 @@
  *   - Activations: x and the intermediate h are stored in the layer's
  *     activation type (bf16 bits or fp32); router weights, combine weights and
  *     outputs are fp32.  Accumulation is fp32.
- *   - Thread safety: no global mutable state; calls on distinct streams with
- *     distinct outputs and workspaces may run concurrently.
+ *   - Thread safety: the only global state is the per-device address of the
+ *     array behind moe_layer_forward_noalloc, looked up once under a lock;
+ *     other calls on distinct streams with distinct outputs and workspaces may
+ *     run concurrently.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -181,6 +183,27 @@ moe_status moe_layer_forward(const moe_layer *layer, const void *x, int32_t T,
                              float *y, void *x_next_opt,
                              int32_t *topk_ids_opt, float *topk_w_opt,
                              void *ws, size_t ws_bytes, void *stream);
+
+/* Size of the device array moe_layer_forward_noalloc uses in place of a
+ * workspace: 16 MiB, enough for about 145 tokens of the 512-expert layer
+ * (hidden 2048, intermediate 768, top-10 + shared, bf16). */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that must not call the allocator).  Same arguments and results as
+ * moe_layer_forward (the same kernels run); the intermediate buffers live in a
+ * library-owned device array of MOE_NOALLOC_SCRATCH_BYTES, one per GPU, held
+ * until the process ends.  The call allocates nothing: the first call on a
+ * device looks the array's address up (with that device current) and keeps
+ * it.  Returns MOE_E_WORKSPACE when the layer needs more than the array at T
+ * tokens (moe_workspace_bytes(layer, T) > MOE_NOALLOC_SCRATCH_BYTES), and
+ * MOE_E_DEVICE if the address lookup fails.  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one device (concurrent streams, threads)
+ * race and must be serialised by the caller. */
+moe_status moe_layer_forward_noalloc(const moe_layer *layer, const void *x, int32_t T,
+                                     float *y, void *x_next_opt,
+                                     int32_t *topk_ids_opt, float *topk_w_opt, void *stream);
 
 /* Bytes of workspace the calls above need for up to T_max tokens (host-only,
  * pure function of the shapes; returns 0 for an invalid descriptor). */

@@ -24,7 +24,7 @@ CODE_BITS = {MOE_Q4_SYM_G32: 4, MOE_Q3_SYM_G32: 3, MOE_Q2_ASYM_G32: 2}
 ACT = {"f32": MOE_ACT_F32, "bf16": MOE_ACT_BF16}
 
 EXPORTS = ("moe_router_topk", "moe_permute", "moe_expert_ffn_q", "moe_expert_gate_up_q", "moe_expert_down_q",
-           "moe_combine", "moe_layer_forward",
+           "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc",
            "moe_workspace_bytes", "moe_stack_forward", "moe_dequant", "moe_status_str", "moe_abi_version")
 
 
@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "moe_expert_down_q": [lp, vp, vp, i32, vp, vp, vp, vp, vp, vp],
             "moe_combine": [lp, vp, vp, vp, vp, i32, vp, vp, vp, vp],
             "moe_layer_forward": [lp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
+            "moe_layer_forward_noalloc": [lp, vp, i32, vp, vp, vp, vp, vp],
             "moe_stack_forward": [lp, i32, vp, i32, vp, vp, sz, vp],
             "moe_dequant": [ctypes.POINTER(c_qmat), i32, i32, i32, vp, vp],
         }
@@ -318,6 +319,21 @@ def _layer_forward_args(layer, x, T, y, x_next, topk_ids, topk_w, ws, stream):
 def moe_layer_forward(layer: Layer, x, T, y, x_next=None, topk_ids=None, topk_w=None, ws=None, stream=None):
     _check("moe_layer_forward", lib().moe_layer_forward(
         *_layer_forward_args(layer, x, T, y, x_next, topk_ids, topk_w, ws, stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_layer_forward_noalloc(layer: Layer, x, T, y, x_next=None, topk_ids=None, topk_w=None, stream=None):
+    """moe_layer_forward with the library's own device array in place of a workspace."""
+    K, H = layer.top_k, layer.hidden
+    _need("y", y, T * H, torch.float32)
+    _need("x_next", x_next, T * H, layer.act_dtype)
+    _need("topk_ids", topk_ids, T * K, torch.int32)
+    _need("topk_w", topk_w, T * K, torch.float32)
+    _check("moe_layer_forward_noalloc", lib().moe_layer_forward_noalloc(
+        layer.ref, _x(layer, x, T), int(T), _p(layer, y), _p(layer, x_next), _p(layer, topk_ids),
+        _p(layer, topk_w), _stream(stream)))
 
 
 class Bound:
