@@ -336,10 +336,10 @@ def batch_figures(spec, layers, T, xpool, ws, y, stream, dev, n_steps, prefix):
 def verify_and_stack(args, dev, q4_layers=None):
     """Extra figures with expert planes filled on the device (2-bit format unless
     stated): the speculative-verify batch (5 tokens through one layer, 16 layer
-    copies rotating), the batch sweep T = 8 .. 256 (2-bit, and 4-bit on the
-    decode copies), and one decode step through the 48-layer stack at batch 1
-    and 8, each with its distinct experts, algorithmic bytes and fraction of
-    8 TB/s."""
+    copies rotating), the batch sweep T = 1 .. 256 in each format (4-bit on the
+    decode copies, 3-bit and 2-bit filled on the device), and one decode step
+    through the 48-layer stack at batch 1 and 8, each with its distinct experts,
+    algorithmic bytes and fraction of 8 TB/s."""
     import torch
 
     import synth
@@ -359,17 +359,20 @@ def verify_and_stack(args, dev, q4_layers=None):
         f"{f['verify_T5_q2_distinct_experts']:.1f}, {100 * f['verify_T5_q2_frac_of_8TBps']:.1f} % of 8 TB/s")
     if not args.no_sweep:
         sweep = {}
-        for fmt, ls, sp in (("q2", vlayers, vs), ("q4", q4_layers, synth.SPECS["decode"])):
+        q3s = synth.SPECS["decode_q3"]
+        q3_layers = [api.Layer(**torch_io.device_filled_kwargs(q3s, c, dev)) for c in range(args.copies)]
+        for fmt, ls, sp in (("q4", q4_layers, synth.SPECS["decode"]), ("q3", q3_layers, q3s), ("q2", vlayers, vs)):
             if ls is None:
                 continue
             xq = xv if fmt == "q2" else torch_io.x_tensor(synth.gen_x(sp, seed=1, tokens=4096).storage, sp.act, dev)
-            for T in (8, 16, 32, 64, 128, 256):
+            for T in (1, 5, 8, 16, 32, 64, 128, 256):
                 g = batch_figures(sp, ls, T, xq, ws, yv, stream, dev, max(20, 1600 // T), f"T{T}")
                 sweep[f"{fmt}_T{T}"] = {k.split("_", 1)[1]: v for k, v in g.items()}
                 log(f"batch sweep {fmt} T={T}: {g[f'T{T}_us_per_step']:.1f} us/step, "
                     f"{g[f'T{T}_tok_s']:.0f} tok/s, U = {g[f'T{T}_distinct_experts']:.1f}, "
                     f"{100 * g[f'T{T}_frac_of_8TBps']:.1f} % of 8 TB/s")
         out["batch_sweep"] = sweep
+        del q3_layers
     del vlayers, ws
     torch.cuda.empty_cache()
 

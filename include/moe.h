@@ -63,8 +63,16 @@ typedef enum moe_status {
  *   MOE_Q2_ASYM_G32: byte j holds elements 4j..4j+3 in bits 1..0, 3..2, 5..4,
  *     7..6 (u in 0..3); w = fp32(s * u + m) with the group's fp16 scale s and
  *     fp16 minimum m.  (2-bit weights: page 3 "A Few Things to Keep in
- *     Perspective".) */
-typedef enum moe_qfmt { MOE_Q4_SYM_G32 = 1, MOE_Q2_ASYM_G32 = 2 } moe_qfmt;
+ *     Perspective".)
+ *   MOE_Q3_SYM_G32: each group of 32 elements is 12 consecutive bytes: bytes
+ *     0..7 hold the two low bits of the codes in the 2-bit layout (element
+ *     4j+i at bits 2i+1..2i of byte j), bytes 8..11 the third bit (element i
+ *     at bit i mod 8 of byte 8 + i div 8); u = low + 4 high (0..7) and
+ *     w = s * (u - 4) with the group's fp16 scale s.  (The pages' 3-bit
+ *     quality tier, page 4 "In brief -- 5 key takeaways" and page 5 "A
+ *     sensible 4090 setup", uses codebook formats the pages do not give; this
+ *     plain symmetric format stands in for it.) */
+typedef enum moe_qfmt { MOE_Q4_SYM_G32 = 1, MOE_Q2_ASYM_G32 = 2, MOE_Q3_SYM_G32 = 3 } moe_qfmt;
 
 /* Storage type of activations x and of the expert intermediate h. */
 typedef enum moe_act { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act;
@@ -72,7 +80,8 @@ typedef enum moe_act { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act;
 /* One packed matrix kind for n experts, rows x cols each, expert e at a fixed
  * stride: codes  [n][rows][cols*bits/8] uint8,
  *         scales [n][rows][cols/32]     fp16 bits,
- *         mins   [n][rows][cols/32]     fp16 bits (2-bit format only, else NULL). */
+ *         mins   [n][rows][cols/32]     fp16 bits (2-bit format only, else NULL).
+ * (bits = 4, 3 or 2; a 3-bit row is cols/32 groups of 12 bytes.) */
 typedef struct moe_qmat {
   const uint8_t *codes;
   const uint16_t *scales;

@@ -72,6 +72,11 @@ __global__ __launch_bounds__(256) void k_dequant(QMat m, int rows, int cols, flo
     const uint32_t byte = m.codes[(size_t)r * (cols / 2) + c / 2];
     const int u = (c & 1) ? (int)(byte >> 4) : (int)(byte & 15u);
     out[idx] = s * (float)(u - 8);
+  } else if constexpr (QF == MOE_Q3_SYM_G32) {
+    const uint8_t* g = m.codes + (size_t)r * (G * 12) + (size_t)(c / kGroup) * 12;
+    const int i = c % kGroup;
+    const int u = (int)(((uint32_t)g[i / 4] >> (2 * (i % 4))) & 3u) | (int)((((uint32_t)g[8 + i / 8] >> (i % 8)) & 1u) << 2);
+    out[idx] = s * (float)(u - 4);
   } else {
     const uint32_t byte = m.codes[(size_t)r * (cols / 4) + c / 4];
     const int u = (int)((byte >> (2 * (c & 3))) & 3u);
@@ -83,8 +88,7 @@ hipError_t launch_dequant(const QMat& m, int qfmt, int rows, int cols, float* ou
   const size_t n = (size_t)rows * cols;
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
-  if (qfmt == MOE_Q4_SYM_G32) k_dequant<MOE_Q4_SYM_G32><<<grid, 256, 0, s>>>(m, rows, cols, out);
-  else k_dequant<MOE_Q2_ASYM_G32><<<grid, 256, 0, s>>>(m, rows, cols, out);
+  by_qfmt(qfmt, [&](auto q) { k_dequant<decltype(q)::value><<<grid, 256, 0, s>>>(m, rows, cols, out); });
   return hipGetLastError();
 }
 

@@ -354,9 +354,9 @@ hipError_t launch_gateup(const FfnArgs& args, hipStream_t s) {
     if (e != hipSuccess || a.mfma_min == 1) return e;
   }
   if (gateup1_ok(a))
-    return a.qfmt == MOE_Q4_SYM_G32 ? gateup1_q<MOE_Q4_SYM_G32>(a, s) : gateup1_q<MOE_Q2_ASYM_G32>(a, s);
+    return by_qfmt(a.qfmt, [&](auto q) { return gateup1_q<decltype(q)::value>(a, s); });
   if (gateup_sb_ok(a)) return launch_gateup_sb(a, s);
-  return a.qfmt == MOE_Q4_SYM_G32 ? dispatch_act<MOE_Q4_SYM_G32>(a, true, s) : dispatch_act<MOE_Q2_ASYM_G32>(a, true, s);
+  return by_qfmt(a.qfmt, [&](auto q) { return dispatch_act<decltype(q)::value>(a, true, s); });
 }
 
 template <int QF> static hipError_t down1_q(const FfnArgs& a, hipStream_t s);
@@ -370,9 +370,9 @@ hipError_t launch_down(const FfnArgs& args, hipStream_t s) {
     const hipError_t e = launch_mfma_down(a, s);
     if (e != hipSuccess || a.mfma_min == 1) return e;
   }
-  if (down1_ok(a)) return a.qfmt == MOE_Q4_SYM_G32 ? down1_q<MOE_Q4_SYM_G32>(a, s) : down1_q<MOE_Q2_ASYM_G32>(a, s);
+  if (down1_ok(a)) return by_qfmt(a.qfmt, [&](auto q) { return down1_q<decltype(q)::value>(a, s); });
   if (down_sb_ok(a)) return launch_down_sb(a, s);
-  return a.qfmt == MOE_Q4_SYM_G32 ? dispatch_act<MOE_Q4_SYM_G32>(a, false, s) : dispatch_act<MOE_Q2_ASYM_G32>(a, false, s);
+  return by_qfmt(a.qfmt, [&](auto q) { return dispatch_act<decltype(q)::value>(a, false, s); });
 }
 
 
@@ -739,8 +739,7 @@ static hipError_t fused_gateup_pl(const RouterArgs& r, const PermuteArgs& pm, co
 
 hipError_t launch_fused_gateup(const RouterArgs& r, const PermuteArgs& pm, const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  return a.qfmt == MOE_Q4_SYM_G32 ? fused_gateup_pl<MOE_Q4_SYM_G32>(r, pm, a, s)
-                                  : fused_gateup_pl<MOE_Q2_ASYM_G32>(r, pm, a, s);
+  return by_qfmt(a.qfmt, [&](auto q) { return fused_gateup_pl<decltype(q)::value>(r, pm, a, s); });
 }
 
 // one wave per slot up to 16 slots (SPW = 1), else two slots per wave;
@@ -776,7 +775,7 @@ static hipError_t down1_q(const FfnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fused_down1(const FfnArgs& a, const CombineArgs& c, hipStream_t s) {
-  return a.qfmt == MOE_Q4_SYM_G32 ? fused_down1_q<MOE_Q4_SYM_G32>(a, c, s) : fused_down1_q<MOE_Q2_ASYM_G32>(a, c, s);
+  return by_qfmt(a.qfmt, [&](auto q) { return fused_down1_q<decltype(q)::value>(a, c, s); });
 }
 
 }  // namespace moe

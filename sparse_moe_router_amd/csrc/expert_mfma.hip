@@ -10,9 +10,11 @@
 // the MFMA consumes the codes themselves and the fp16 group scale is applied
 // in fp32 after each K = 32 step, which is exactly one group.  A code u is
 // OR-ed into the top mantissa bits of bf16 1.0, giving the exact bf16 value
-// 1 + u / 16 (4-bit) or 1 + u / 4 (2-bit); with bf16 x every product is exact
-// in fp32, and the offset term enters through the MFMA's accumulator input:
+// 1 + u / 16 (4-bit), 1 + u / 8 (3-bit) or 1 + u / 4 (2-bit); with bf16 x every
+// product is exact in fp32, and the offset term enters through the MFMA's
+// accumulator input:
 //   4-bit:  D = sum (1 + u/16) x - 1.5 sum x = sum (u - 8) x / 16,  acc += 16 s D
+//   3-bit:  D = sum (1 + u/8) x - 1.5 sum x  = sum (u - 4) x / 8,   acc += 8 s D
 //   2-bit:  D = sum (1 + u/4) x - sum x      = sum u x / 4,         acc += 4 s D + m sum x
 // Keeping the code in the top mantissa bits keeps the cancelled offset within
 // a few times the signal, so the fp32 sums lose little to the cancellation.
@@ -45,7 +47,9 @@ __device__ __forceinline__ f32x4_t mfma16(const uint32_t (&a)[4], const uint32_t
                                                  c, 0, 0, 0);
 }
 
-// 8 codes of one B lane -> 4 bf16 pairs (k_j, k_{j+4}): 1 + u/16 (4-bit) or 1 + u/4 (2-bit).
+// 8 codes of one B lane -> 4 bf16 pairs (k_j, k_{j+4}): 1 + u/16 (4-bit),
+// 1 + u/8 (3-bit: w holds the 8 low-bit fields in bits 0..15 and the 8 third
+// bits in bits 16..23) or 1 + u/4 (2-bit).
 template <int QF>
 __device__ __forceinline__ void unpack_b(uint32_t w, uint32_t (&b)[4]) {
   asm volatile("" : "+v"(w));  // unpack at the point of use
@@ -54,6 +58,15 @@ __device__ __forceinline__ void unpack_b(uint32_t w, uint32_t (&b)[4]) {
     b[1] = and_or(w >> 1, 0x00780078u, 0x3f803f80u);
     b[2] = and_or(w >> 5, 0x00780078u, 0x3f803f80u);
     b[3] = and_or(w >> 9, 0x00780078u, 0x3f803f80u);
+  } else if constexpr (QF == MOE_Q3_SYM_G32) {
+    // low fields 0..3 -> bits 0..7, 4..7 -> bits 16..23; third bits 0..3 ->
+    // bits 0..3, 4..7 -> bits 16..19; field j -> bits 4..5, third bit j -> bit 6
+    const uint32_t s = (w & 0xffu) | ((w & 0xff00u) << 8);
+    const uint32_t h = ((w >> 16) & 0xfu) | ((w >> 4) & 0xf0000u);
+    b[0] = and_or(h << 6, 0x00400040u, and_or(s << 4, 0x00300030u, 0x3f803f80u));
+    b[1] = and_or(h << 5, 0x00400040u, and_or(s << 2, 0x00300030u, 0x3f803f80u));
+    b[2] = and_or(h << 4, 0x00400040u, and_or(s, 0x00300030u, 0x3f803f80u));
+    b[3] = and_or(h << 3, 0x00400040u, and_or(s >> 2, 0x00300030u, 0x3f803f80u));
   } else {  // 16 bits = 8 crumbs; the second byte moves to bits 16..23, crumb j -> bits 5..6
     const uint32_t s = (w & 0xffu) | ((w & 0xff00u) << 8);
     b[0] = and_or(s << 5, 0x00600060u, 0x3f803f80u);
@@ -186,7 +199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       sx1 = dot2_bf16(0x3f803f80u, p.w, sx1);
     }
     const float sx = sx0 + sx1;
-    s_c[buf][jg][r] = QF == MOE_Q4_SYM_G32 ? -1.5f * sx : -sx;
+    s_c[buf][jg][r] = QF == MOE_Q2_ASYM_G32 ? -sx : -1.5f * sx;
   };
 
   // ---- weights: the block's 256 row slots (NMAT x 64 WN rows) of codes and
@@ -196,10 +209,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // nblk * 64 WN + s % (64 WN) (clamped to the last row; never stored).
   //   4-bit codes: per 16 slots 1 KiB laid out [group q][slot][16 B]
   //   2-bit codes: per 32 slots 1 KiB laid out [group pair p][slot][16 B]
+  //   3-bit codes: per 64 slots 3 KiB laid out [16-byte part q of the
+  //                chunk's 48 bytes][slot][16 B]
   //   scales / minima: [slot][4 x fp16]
   // With these layouts the MFMA lanes' reads below hit 64 distinct banks.
   constexpr int kSlots = NMAT * 64 * WN;  // 256
-  constexpr int kCodeChunk = QF == MOE_Q4_SYM_G32 ? 64 : 32;  // code bytes per row per chunk
+  constexpr int kCodeChunk = kChunkG * code_bits(QF) * 4;  // code bytes per row per chunk: 64, 48, 32
   __shared__ __align__(16) uint8_t s_b[2][kSlots * kCodeChunk];
   __shared__ __align__(16) uint16_t s_s[2][kSlots * kChunkG];
   __shared__ __align__(16) uint16_t s_m[QF == MOE_Q2_ASYM_G32 ? 2 : 1][QF == MOE_Q2_ASYM_G32 ? kSlots * kChunkG : 8];
@@ -207,7 +222,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 15, lc = lane >> 4;
   const int eidx = shared ? 0 : expert;
-  constexpr int kCodeBytesPerGroup = QF == MOE_Q4_SYM_G32 ? 16 : 8;
+  constexpr int kCodeBytesPerGroup = code_bits(QF) * 4;
   const uint32_t row_bytes = (uint32_t)G * kCodeBytesPerGroup;
   // the expert's matrices (uniform); pick field by field, since a reference
   // into the argument block would force it into scratch
@@ -237,17 +252,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
   auto slot_row = [&](int slot) { return (uint32_t)min(nblk * 64 * WN + slot % (64 * WN), rows - 1); };
   // This wave's DMA sources: 4-bit codes, 4 instructions of 16 slots (lane ->
-  // slot 16 i + lane % 16, group lane / 16); 2-bit codes, 2 of 32 slots (lane
-  // -> slot 32 i + lane % 32, group pair lane / 32); scales (minima), 2 of 32
-  // slots (lane -> slot 32 i + lane / 2, group pair lane % 2).  Byte offsets
-  // within the chunk's first group; matrix per instruction (uniform).
-  constexpr int kCodeInst = QF == MOE_Q4_SYM_G32 ? 4 : 2;
+  // slot 16 i + lane % 16, group lane / 16); 3-bit codes, 3 of 64 slots
+  // (instruction 3 w + i: slots 64 ((3 w + i) / 3) + lane, 16-byte part
+  // (3 w + i) % 3); 2-bit codes, 2 of 32 slots (lane -> slot 32 i + lane % 32,
+  // group pair lane / 32); scales (minima), 2 of 32 slots (lane -> slot
+  // 32 i + lane / 2, group pair lane % 2).  Byte offsets within the chunk's
+  // first group; matrix per instruction (uniform).
+  constexpr int kCodeInst = code_bits(QF);
   uint32_t code_off[kCodeInst], scale_off[2];
 #pragma unroll
   for (int i = 0; i < kCodeInst; ++i) {
     if constexpr (QF == MOE_Q4_SYM_G32) {
       const int slot = (wave * 4 + i) * 16 + (lane & 15);
       code_off[i] = slot_row(slot) * row_bytes + (uint32_t)(lane >> 4) * 16;
+    } else if constexpr (QF == MOE_Q3_SYM_G32) {
+      const int blk = wave * 3 + i;
+      const int slot = (blk / 3) * 64 + lane;
+      code_off[i] = slot_row(slot) * row_bytes + (uint32_t)(blk % 3) * 16;
     } else {
       const int slot = (wave * 2 + i) * 32 + (lane & 31);
       code_off[i] = slot_row(slot) * row_bytes + (uint32_t)(lane >> 5) * 16;
@@ -262,7 +283,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int i = 0; i < kCodeInst; ++i) {
       const int blk = wave * kCodeInst + i;  // 1 KiB block of the chunk buffer
-      const int mi = (blk * (QF == MOE_Q4_SYM_G32 ? 16 : 32)) / (64 * WN);
+      const int mi = QF == MOE_Q3_SYM_G32 ? ((blk / 3) * 64) / (64 * WN)
+                                          : (blk * (QF == MOE_Q4_SYM_G32 ? 16 : 32)) / (64 * WN);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(cb[mi] + code_off[i] + (uint32_t)kc * kCodeChunk),
                                        static_cast<void*>(&s_b[buf][blk * 1024]), 16, 0, 0);
     }
@@ -324,6 +346,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           const int slot = slot_of(mi, nt);
           if constexpr (QF == MOE_Q4_SYM_G32) {
             g.bw[mi][nt] = *reinterpret_cast<const uint32_t*>(&s_b[buf][(slot >> 4) * 1024 + j * 256 + (slot & 15) * 16 + lc * 4]);
+          } else if constexpr (QF == MOE_Q3_SYM_G32) {
+            // the lane's 8 codes: low-bit bytes 12 j + 2 lc, + 1 and third-bit byte 12 j + 8 + lc of the chunk
+            const uint8_t* base = &s_b[buf][(slot >> 6) * 3072 + (slot & 63) * 16];
+            const int o1 = 12 * j + 2 * lc, o2 = 12 * j + 8 + lc;
+            const uint32_t lo = *reinterpret_cast<const uint16_t*>(base + (o1 >> 4) * 1024 + (o1 & 15));
+            const uint32_t hi = base[(o2 >> 4) * 1024 + (o2 & 15)];
+            g.bw[mi][nt] = lo | (hi << 16);
           } else {
             g.bw[mi][nt] = *reinterpret_cast<const uint16_t*>(
                 &s_b[buf][(slot >> 5) * 1024 + (j >> 1) * 512 + (slot & 31) * 16 + (j & 1) * 8 + lc * 2]);
@@ -417,7 +446,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   else chunks(std::integral_constant<int, 4>{});
 
   // ---- epilogue: D lane l holds token rows 4 (l / 16) + i of each M tile, column ln
-  constexpr float kUnit = QF == MOE_Q4_SYM_G32 ? 16.f : 4.f;  // the codes' 1/16 or 1/4, exactly
+  constexpr float kUnit = QF == MOE_Q4_SYM_G32 ? 16.f : QF == MOE_Q3_SYM_G32 ? 8.f : 4.f;  // the codes' 1/16, 1/8, 1/4
   const bool all_rows = (nblk + 1) * (64 * WN) <= rows;  // uniform: no row of this block is past the end
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -491,8 +520,7 @@ hipError_t launch_mfma_gateup(const FfnArgs& a, hipStream_t s) {
   const int nb = (a.I + 127) / 128;  // 4 waves x 2 N tiles of 16 rows of I
   const int64_t unit = (int64_t)8 * kXcdTiles * nb;
   const dim3 grid((unsigned)(((int64_t)nb * tile_capacity(a, ws) + unit - 1) / unit * unit));
-  if (a.qfmt == MOE_Q4_SYM_G32) k_expert_mfma<MOE_Q4_SYM_G32, 2, 2><<<grid, 256, 0, s>>>(a, ws, nb);
-  else k_expert_mfma<MOE_Q2_ASYM_G32, 2, 2><<<grid, 256, 0, s>>>(a, ws, nb);
+  by_qfmt(a.qfmt, [&](auto q) { k_expert_mfma<decltype(q)::value, 2, 2><<<grid, 256, 0, s>>>(a, ws, nb); });
   return hipGetLastError();
 }
 
@@ -501,8 +529,7 @@ hipError_t launch_mfma_down(const FfnArgs& a, hipStream_t s) {
   const int nb = (a.H + 255) / 256;  // 4 waves x 4 N tiles of 16 rows of H
   const int64_t unit = (int64_t)8 * kXcdTiles * nb;
   const dim3 grid((unsigned)(((int64_t)nb * tile_capacity(a, ws) + unit - 1) / unit * unit));
-  if (a.qfmt == MOE_Q4_SYM_G32) k_expert_mfma<MOE_Q4_SYM_G32, 1, 4><<<grid, 256, 0, s>>>(a, ws, nb);
-  else k_expert_mfma<MOE_Q2_ASYM_G32, 1, 4><<<grid, 256, 0, s>>>(a, ws, nb);
+  by_qfmt(a.qfmt, [&](auto q) { k_expert_mfma<decltype(q)::value, 1, 4><<<grid, 256, 0, s>>>(a, ws, nb); });
   return hipGetLastError();
 }
 

@@ -199,8 +199,7 @@ bool down_sb_ok(const FfnArgs& a) {
 hipError_t launch_gateup_sb(const FfnArgs& a, hipStream_t s) {
   const int ny = a.T * a.K;
   const dim3 grid((a.I + 4 * kSbRpw - 1) / (4 * kSbRpw), ny + (a.n_shared && a.hs ? 1 : 0));
-  if (a.qfmt == MOE_Q4_SYM_G32) k_gateup_sb<MOE_Q4_SYM_G32><<<grid, 256, 0, s>>>(a, ny);
-  else k_gateup_sb<MOE_Q2_ASYM_G32><<<grid, 256, 0, s>>>(a, ny);
+  by_qfmt(a.qfmt, [&](auto q) { k_gateup_sb<decltype(q)::value><<<grid, 256, 0, s>>>(a, ny); });
   return hipGetLastError();
 }
 
@@ -210,13 +209,11 @@ hipError_t launch_down_sb(const FfnArgs& a, hipStream_t s) {
   const dim3 grid((a.H + 31) / 32, ny + (a.n_shared && a.so ? 1 : 0));
   const size_t lds = (size_t)kSbTok * 17 * G * 4;
   auto go = [&](auto kern) { kern<<<grid, 256, lds, s>>>(a, ny); };
-  if (a.qfmt == MOE_Q4_SYM_G32) {
-    if (gpl <= 1) go(k_down_sb<MOE_Q4_SYM_G32, 1>); else if (gpl == 2) go(k_down_sb<MOE_Q4_SYM_G32, 2>);
-    else if (gpl == 3) go(k_down_sb<MOE_Q4_SYM_G32, 3>); else go(k_down_sb<MOE_Q4_SYM_G32, 4>);
-  } else {
-    if (gpl <= 1) go(k_down_sb<MOE_Q2_ASYM_G32, 1>); else if (gpl == 2) go(k_down_sb<MOE_Q2_ASYM_G32, 2>);
-    else if (gpl == 3) go(k_down_sb<MOE_Q2_ASYM_G32, 3>); else go(k_down_sb<MOE_Q2_ASYM_G32, 4>);
-  }
+  by_qfmt(a.qfmt, [&](auto q) {
+    constexpr int QF = decltype(q)::value;
+    if (gpl <= 1) go(k_down_sb<QF, 1>); else if (gpl == 2) go(k_down_sb<QF, 2>);
+    else if (gpl == 3) go(k_down_sb<QF, 3>); else go(k_down_sb<QF, 4>);
+  });
   return hipGetLastError();
 }
 

@@ -120,6 +120,13 @@ __device__ __forceinline__ void unpack_group(const typename CodeOf<QF>::T& cw, u
       b[4 * i + 2] = and_or(w >> 5, 0x00780078u, 0x3f803f80u);
       b[4 * i + 3] = and_or(w >> 9, 0x00780078u, 0x3f803f80u);
     }
+  } else if constexpr (QF == MOE_Q3_SYM_G32) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t hs = q3_high(cw[2], i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[8 * i + j] = q3_pair(cw[i], hs, j);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -143,7 +150,7 @@ __device__ __forceinline__ float group_acc_unpacked(float acc, const uint32_t (&
     d1 = dot2_bf16(b[i + 1], x.p[i + 1], d1);
   }
   const float d = (d0 + d1) - x.c;
-  constexpr float kUnit = QF == MOE_Q4_SYM_G32 ? 16.f : 4.f;
+  constexpr float kUnit = QF == MOE_Q4_SYM_G32 ? 16.f : QF == MOE_Q3_SYM_G32 ? 8.f : 4.f;
   acc = fmaf(f16_to_f32(s16) * kUnit, d, acc);
   if constexpr (QF == MOE_Q2_ASYM_G32) acc = fmaf(f16_to_f32(m16), x.sx, acc);
   return acc;

@@ -3,17 +3,21 @@
 //
 // Inner product of one group (bf16 activations): each code u is OR-ed into the
 // top mantissa bits of bf16 1.0, giving the exact bf16 number 1 + u/16 (4-bit)
-// or 1 + u/4 (2-bit), two codes per 32-bit word, and v_dot2_f32_bf16 multiplies
-// the pair with a pair of activations in fp32 (every product is exact).  The
-// offset is removed with a per-group constant computed once per token:
+// 1 + u/8 (3-bit) or 1 + u/4 (2-bit), two codes per 32-bit word, and
+// v_dot2_f32_bf16 multiplies the pair with a pair of activations in fp32
+// (every product is exact).  The offset is removed with a per-group constant
+// computed once per token:
 //   4-bit:  D = sum (1 + u/16) x - 1.5 sum x = sum (u - 8) x / 16,  acc += 16 s D
+//   3-bit:  D = sum (1 + u/8) x - 1.5 sum x  = sum (u - 4) x / 8,   acc += 8 s D
 //   2-bit:  D = sum (1 + u/4) x - sum x      = sum u x / 4,         acc += 4 s D + m sum x
 // (w = s q with q = u - 8, or w = s u + m).  With the code in the top mantissa
 // bits the cancelled offset stays within a few times the signal, so the fp32
 // sums lose little to the cancellation.  Activation pairs are pre-arranged per
 // token to match the code pairs a mask and a shift produce: 4-bit word i of a
 // group yields pairs (8i+j, 8i+4+j) for j = 0..3 from nibbles j and j+4; 2-bit
-// word i yields pairs (16i+j, 16i+8+j) for j = 0..7 from crumbs j and j+8.
+// word i yields pairs (16i+j, 16i+8+j) for j = 0..7 from crumbs j and j+8, and
+// so does 3-bit low-bit word i together with bits 16i+j, 16i+8+j of the
+// third-bit word.
 #pragma once
 
 #include "moe_device.h"
@@ -23,10 +27,12 @@ namespace moe {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 template <int QF> struct CodeOf;
 template <> struct CodeOf<MOE_Q4_SYM_G32> { using T = u32x4; static constexpr int kBytes = 16; };
 template <> struct CodeOf<MOE_Q2_ASYM_G32> { using T = u32x2; static constexpr int kBytes = 8; };
+template <> struct CodeOf<MOE_Q3_SYM_G32> { using T = u32x3; static constexpr int kBytes = 12; };
 
 // Prepared activations of one 32-element group of one token.
 template <int QF, int ACT> struct XGroup;
@@ -34,7 +40,7 @@ template <int QF, int ACT> struct XGroup;
 template <int QF> struct XGroup<QF, MOE_ACT_BF16> {
   uint4 q[4];      // the group's 32 raw bf16 values
   uint32_t p[16];  // bf16 pairs matching the code pairs
-  float c;         // 1.5 sum x (4-bit) or sum x (2-bit)
+  float c;         // 1.5 sum x (4-bit, 3-bit) or sum x (2-bit)
   float sx;        // sum x (2-bit only)
 
   __device__ __forceinline__ void load_raw(const void* base, size_t elem) {
@@ -63,7 +69,7 @@ template <int QF> struct XGroup<QF, MOE_ACT_BF16> {
         }
       }
     }
-    constexpr uint32_t kOff = (QF == MOE_Q4_SYM_G32) ? 0x3fc03fc0u : 0x3f803f80u;  // (1.5, 1.5) / (1, 1)
+    constexpr uint32_t kOff = (QF == MOE_Q2_ASYM_G32) ? 0x3f803f80u : 0x3fc03fc0u;  // (1, 1) / (1.5, 1.5)
     float c0 = 0.f, c1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
@@ -108,6 +114,22 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
 // Crumb j (bits 2j, 2j+1) moved to bits 5..6 (and crumb j + 8 to bits 21..22).
 __device__ __forceinline__ uint32_t shift_crumb(uint32_t w, int j) { return j <= 2 ? w << (5 - 2 * j) : w >> (2 * j - 5); }
 
+// The third bits of 3-bit low-bit word i (elements 16i .. 16i + 15 of the
+// group: bits 16i .. 16i + 15 of the third-bit word t), spread so that
+// element 16i + j sits at bit j and element 16i + 8 + j at bit 16 + j.
+__device__ __forceinline__ uint32_t q3_high(uint32_t t, int i) {
+  return __builtin_amdgcn_perm(t, t, i == 0 ? 0x0c010c00u : 0x0c030c02u);
+}
+
+// Codes j and j + 8 of 3-bit low-bit word w (crumbs at bits 2j and 2j + 16)
+// with their third bits (bits j and 16 + j of the spread word hs) -> the bf16
+// pair (1 + u/8): low bits to 4..5 and 20..21, third bit to 6 and 22.
+__device__ __forceinline__ uint32_t q3_pair(uint32_t w, uint32_t hs, int j) {
+  const uint32_t lo = j <= 2 ? w << (4 - 2 * j) : w >> (2 * j - 4);
+  const uint32_t hi = j <= 6 ? hs << (6 - j) : hs >> (j - 6);
+  return and_or(hi, 0x00400040u, and_or(lo, 0x00300030u, 0x3f803f80u));
+}
+
 // bf16 activations: sum q x / 16 (4-bit, q = u - 8) or sum u x / 4 (2-bit);
 // fp32 activations: sum q x or sum u x.
 template <int QF, int ACT>
@@ -126,6 +148,19 @@ __device__ __forceinline__ float group_dot(const typename CodeOf<QF>::T& cw, con
         d1 = dot2_bf16(and_or(w[i] >> 1, 0x00780078u, 0x3f803f80u), x.p[4 * i + 1], d1);
         d0 = dot2_bf16(and_or(w[i] >> 5, 0x00780078u, 0x3f803f80u), x.p[4 * i + 2], d0);
         d1 = dot2_bf16(and_or(w[i] >> 9, 0x00780078u, 0x3f803f80u), x.p[4 * i + 3], d1);
+      }
+    } else if constexpr (QF == MOE_Q3_SYM_G32) {
+      uint32_t w[3] = {cw[0], cw[1], cw[2]};
+#pragma unroll
+      for (int i = 0; i < 3; ++i) asm volatile("" : "+v"(w[i]));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t hs = q3_high(w[2], i);
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          d0 = dot2_bf16(q3_pair(w[i], hs, j), x.p[8 * i + j], d0);
+          d1 = dot2_bf16(q3_pair(w[i], hs, j + 1), x.p[8 * i + j + 1], d1);
+        }
       }
     } else {
       uint32_t w[2] = {cw[0], cw[1]};
@@ -153,6 +188,19 @@ __device__ __forceinline__ float group_dot(const typename CodeOf<QF>::T& cw, con
           d1 = fmaf((float)((int)((w[i] >> (4 * j + 4)) & 15u) - 8), x.at(8 * i + j + 1), d1);
         }
       }
+    } else if constexpr (QF == MOE_Q3_SYM_G32) {
+      const uint32_t w[3] = {cw[0], cw[1], cw[2]};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          const int e = 16 * i + j;
+          const int u0 = (int)(((w[i] >> (2 * j)) & 3u) | (((w[2] >> e) & 1u) << 2));
+          const int u1 = (int)(((w[i] >> (2 * j + 2)) & 3u) | (((w[2] >> (e + 1)) & 1u) << 2));
+          d0 = fmaf((float)(u0 - 4), x.at(e), d0);
+          d1 = fmaf((float)(u1 - 4), x.at(e + 1), d1);
+        }
+      }
     } else {
       const uint32_t w[2] = {cw[0], cw[1]};
 #pragma unroll
@@ -172,8 +220,8 @@ template <int QF, int ACT>
 __device__ __forceinline__ float group_acc(float acc, const typename CodeOf<QF>::T& cw, uint16_t s16, uint16_t m16,
                                            const XGroup<QF, ACT>& x) {
   const float d = group_dot<QF, ACT>(cw, x);
-  // the bf16 path's sums carry a factor 1/16 or 1/4, folded into the scale (exactly)
-  constexpr float kUnit = ACT == MOE_ACT_BF16 ? (QF == MOE_Q4_SYM_G32 ? 16.f : 4.f) : 1.f;
+  // the bf16 path's sums carry a factor 1/16, 1/8 or 1/4, folded into the scale (exactly)
+  constexpr float kUnit = ACT == MOE_ACT_BF16 ? (QF == MOE_Q4_SYM_G32 ? 16.f : QF == MOE_Q3_SYM_G32 ? 8.f : 4.f) : 1.f;
   acc = fmaf(f16_to_f32(s16) * kUnit, d, acc);
   if constexpr (QF == MOE_Q2_ASYM_G32) acc = fmaf(f16_to_f32(m16), x.sx, acc);
   return acc;
@@ -190,7 +238,7 @@ struct MatView {
 template <int QF>
 __device__ __forceinline__ MatView expert_view(const QMat& m, int e, int rows, int cols) {
   MatView v;
-  v.row_bytes = (size_t)cols * (QF == MOE_Q4_SYM_G32 ? 4 : 2) / 8;
+  v.row_bytes = (size_t)cols * code_bits(QF) / 8;
   v.groups = cols / kGroup;
   v.codes = m.codes + (size_t)e * rows * v.row_bytes;
   v.scales = m.scales + (size_t)e * rows * v.groups;

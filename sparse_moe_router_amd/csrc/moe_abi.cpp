@@ -13,7 +13,7 @@ using namespace moe;
 
 constexpr int kMaxDim = 4096;
 constexpr int kMaxExperts = 8192;
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -32,7 +32,7 @@ moe_status check_layer(const moe_layer* L) {
   if (L->hidden > kMaxDim || L->inter > kMaxDim) return MOE_E_UNSUPPORTED;
   if (L->n_experts < 1 || L->top_k < 1 || L->top_k > L->n_experts) return MOE_E_ARG;
   if (L->n_experts > kMaxExperts) return MOE_E_UNSUPPORTED;
-  if (L->qfmt != MOE_Q4_SYM_G32 && L->qfmt != MOE_Q2_ASYM_G32) return MOE_E_UNSUPPORTED;
+  if (L->qfmt != MOE_Q4_SYM_G32 && L->qfmt != MOE_Q2_ASYM_G32 && L->qfmt != MOE_Q3_SYM_G32) return MOE_E_UNSUPPORTED;
   if (L->act != MOE_ACT_F32 && L->act != MOE_ACT_BF16) return MOE_E_UNSUPPORTED;
   if (!L->router_w || !aligned(L->router_w, 16)) return MOE_E_ARG;
   if (L->routed.n != L->n_experts) return MOE_E_ARG;
@@ -312,7 +312,7 @@ moe_status moe_stack_forward(const moe_layer* layers, int32_t n_layers, void* x_
 
 moe_status moe_dequant(const moe_qmat* m, int32_t qfmt, int32_t rows, int32_t cols, float* out, void* stream) {
   if (!m || !out || rows < 0 || cols < 0 || cols % kGroup) return MOE_E_ARG;
-  if (qfmt != MOE_Q4_SYM_G32 && qfmt != MOE_Q2_ASYM_G32) return MOE_E_UNSUPPORTED;
+  if (qfmt != MOE_Q4_SYM_G32 && qfmt != MOE_Q2_ASYM_G32 && qfmt != MOE_Q3_SYM_G32) return MOE_E_UNSUPPORTED;
   if (!m->codes || !m->scales || (qfmt == MOE_Q2_ASYM_G32 && !m->mins)) return MOE_E_ARG;
   return dev(launch_dequant(qmat(*m), qfmt, rows, cols, out, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -5,11 +5,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe.h"
 
 namespace moe {
 
 constexpr int kGroup = 32;
+
+// Code bits per weight of a format.
+__host__ __device__ constexpr int code_bits(int qfmt) {
+  return qfmt == MOE_Q4_SYM_G32 ? 4 : qfmt == MOE_Q3_SYM_G32 ? 3 : 2;
+}
+
+// f(std::integral_constant<int, QF>{}) for the layer's format (one template
+// instance per format).
+template <typename F>
+inline auto by_qfmt(int qfmt, F&& f) {
+  if (qfmt == MOE_Q4_SYM_G32) return f(std::integral_constant<int, MOE_Q4_SYM_G32>{});
+  if (qfmt == MOE_Q3_SYM_G32) return f(std::integral_constant<int, MOE_Q3_SYM_G32>{});
+  return f(std::integral_constant<int, MOE_Q2_ASYM_G32>{});
+}
 
 struct QMat {
   const uint8_t* codes;

@@ -69,6 +69,7 @@ def _spec_table() -> dict:
         "tiny": LayerSpec("tiny", 64, 8, 2, 128, 4, Q4, ACT_F32, 0.02, None, family=0),
         "decode": LayerSpec("decode", h, e, k, i, 1, Q4, ACT_BF16, rstd, 1.1, family=1),
         "verify": LayerSpec("verify", h, e, k, i, 5, Q2, ACT_BF16, rstd, 1.1, family=2),
+        "decode_q3": LayerSpec("decode_q3", h, e, k, i, 1, Q3, ACT_BF16, rstd, 1.1, family=5),
         "prefill": LayerSpec("prefill", h, e, k, i, 4096, Q4, ACT_BF16, rstd, 1.1, family=1),
         "stack_t1": LayerSpec("stack_t1", h, e, k, i, 1, Q2, ACT_BF16, rstd, 1.1, family=4, n_layers=48),
         "stack_t8": LayerSpec("stack_t8", h, e, k, i, 8, Q2, ACT_BF16, rstd, 1.1, family=4, n_layers=48),

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert api.moe_abi_version() == 1
+    assert api.moe_abi_version() == 2
     for s in range(5):
         assert api.lib().moe_status_str(s).startswith(b"MOE_")
 
@@ -82,6 +82,13 @@ def test_q2_requires_mins():
     assert ws_bytes(L, 1) > 0
     L.routed.down.mins = None
     assert ws_bytes(L, 1) == 0
+
+
+def test_q3_format_accepted_without_mins():
+    L = layer(qfmt=api.MOE_Q3_SYM_G32)
+    assert ws_bytes(L, 1) > 0
+    q = api.c_qmat(FAKE, FAKE, None)
+    assert api.lib().moe_dequant(ctypes.byref(q), api.MOE_Q3_SYM_G32, 4, 33, FAKE, None) == api.MOE_E_ARG
 
 
 def test_token_count_rules():

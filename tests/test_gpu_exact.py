@@ -43,11 +43,11 @@ def _t(a):
 DOWN_PATHS = [
     ("one_token", 1, 10, 16, 2048, 768, "bf16"),      # k_down1
     ("small_batch", 8, 4, 8, 2048, 768, "bf16"),      # k_down_sb (T K <= 256)
-    ("gemv", 100, 3, 64, 256, 768, "bf16"),           # k_down (T K > 256, < 8 tokens per expert)
+    ("gemv", 100, 3, 64, 160, 768, "bf16"),           # k_down (T K > 256, H not a multiple of 128)
     ("gemv_f32", 20, 3, 8, 256, 768, "f32"),          # k_down, fp32 activations
     ("grouped_gemm", 512, 2, 8, 256, 768, "bf16"),    # k_expert_mfma (>= 8 tokens per expert)
 ]
-FORMATS = ["q4_sym_g32", "q2_asym_g32"]
+FORMATS = ["q4_sym_g32", "q3_sym_g32", "q2_asym_g32"]
 
 
 def _routing(T, K, E, seed):
@@ -142,7 +142,7 @@ TIE_CASES = [
     ("fused_few_tokens_k20", 512, 20, 1, "forward"),  # k_fused_gateup (K > 16)
     ("route_small", 512, 10, 5, "forward"),           # k_route_small (T K <= 256)
     ("topk_regs_fp32_router", 512, 10, 3, "router"),  # k_router_logits + k_topk_regs
-    ("topk_regs_mfma_router", 512, 10, 40, "router"), # k_router_mfma + k_topk_regs
+    ("topk_regs_mfma_router", 512, 10, 130, "router"),  # k_router_mfma + k_topk_regs
     ("topk_lds", 1500, 10, 4, "router"),              # E > 1024: k_topk_lds
 ]
 

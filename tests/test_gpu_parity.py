@@ -99,6 +99,18 @@ def test_dequant_q2_grid():
     assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
 
 
+def test_dequant_q3_exhaustive():
+    sb = _finite_f16()
+    u = np.tile(np.tile(np.arange(8, dtype=np.uint8), 4), (sb.size, 1))
+    codes = synth.pack_q3(u)
+    out = torch.empty((sb.size, 32), dtype=torch.float32, device=gu.DEV)
+    c = torch.from_numpy(codes).to(gu.DEV)
+    s = torch.from_numpy(sb[:, None].view(np.int16).copy()).to(gu.DEV)
+    api.moe_dequant(c, s, None, "q3_sym_g32", sb.size, 32, out)
+    want = mo.dequant_q3(codes, sb[:, None])
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
+
+
 def test_dequant_real_expert_rows():
     spec = synth.SPECS["verify"]
     es = synth.gen_experts(spec, [7], threads=1)
@@ -144,7 +156,14 @@ CASES = [
     (64, 96, 8, 8, 1, "q2_asym_g32", "bf16", False),
     (128, 1024, 20, 16, 1, "q4_sym_g32", "bf16", True),       # K = 16 slots, I = 1024
     (2048, 768, 64, 10, 25, "q4_sym_g32", "bf16", True),     # small-batch kernels at T K = 250 (<= 256)
-    (2048, 768, 64, 10, 26, "q2_asym_g32", "bf16", True),     # T K = 260: the per-expert GEMV kernels
+    (2048, 768, 64, 10, 26, "q2_asym_g32", "bf16", True),     # T K = 260: the grouped GEMM
+    (96, 160, 13, 3, 7, "q3_sym_g32", "bf16", True),          # 3-bit: ragged shapes, small-batch kernels
+    (2048, 768, 16, 4, 9, "q3_sym_g32", "bf16", True),
+    (4096, 96, 6, 2, 5, "q3_sym_g32", "f32", True),           # fp32 activations, two groups per lane
+    (224, 352, 30, 6, 33, "q3_sym_g32", "f32", True),         # per-expert GEMV, fp32 activations
+    (128, 64, 300, 7, 700, "q3_sym_g32", "bf16", True),       # multi-block permutation
+    (96, 160, 13, 3, 1, "q3_sym_g32", "bf16", True),          # one token: fused down + combine
+    (2048, 768, 64, 10, 25, "q3_sym_g32", "bf16", True),      # small-batch kernels at the layer's row shapes
     (64, 64, 1500, 3, 4, "q4_sym_g32", "bf16", True),         # E > 1024: top-k from LDS
     (96, 64, 1024, 70, 3, "q2_asym_g32", "bf16", True),       # K > 64 slots per token
     (64, 64, 8192, 64, 3, "q4_sym_g32", "bf16", True),        # the most experts the ABI takes, K = 64
@@ -173,6 +192,8 @@ MFMA_CASES = [
     (640, 384, 16, 4, 300, "q4_sym_g32", False),
     (2048, 768, 32, 8, 160, "q4_sym_g32", True),    # the layer's row shapes
     (2048, 768, 32, 8, 160, "q2_asym_g32", True),
+    (640, 384, 16, 4, 300, "q3_sym_g32", True),     # 3-bit: odd chunk counts, ragged down rows
+    (2048, 768, 32, 8, 160, "q3_sym_g32", True),
     (128, 256, 3, 3, 70, "q4_sym_g32", True),       # K = E: every expert takes every token
 ]
 
@@ -541,16 +562,25 @@ def family2():
     return ld, gu.device_layer(ld)
 
 
-@pytest.mark.parametrize("fmt", ["q4", "q2"])
-@pytest.mark.parametrize("T", [16, 64, 256])
-def test_batched_decode_512_experts(T, fmt, family1, family2):
+@pytest.fixture(scope="module")
+def family3():
+    spec = synth.SPECS["decode_q3"]
+    gu.say("generating the 512-expert 3-bit layer")
+    ld = synth.gen_layer(spec)
+    return ld, gu.device_layer(ld)
+
+
+@pytest.mark.parametrize("fmt", ["q4", "q3", "q2"])
+@pytest.mark.parametrize("T", [1, 5, 16, 64, 256])
+def test_batched_decode_512_experts(T, fmt, family1, family2, family3):
     """Batches of T decode tokens through the 512-expert top-10 + shared layer
-    (H 2048, I 768): T = 16 takes the small-batch kernels, T = 64 and 256 the
-    grouped GEMMs (routing by the fp32 pass at 64, on the matrix cores at 256).
+    (H 2048, I 768) in each weight format: T = 1 the fused one-token kernels,
+    T = 5 and 16 the small-batch kernels, T = 64 and 256 the grouped GEMMs
+    (routing by the fp32 pass at 64, on the matrix cores at 256).
     Routing, permutation, every certified h flip, y and the per-pair outputs
     against the oracle fed the GPU's certified h; y against the oracle's own
     rounding is reported; moe_layer_forward gives the bits of the split calls."""
-    ld, L = family1 if fmt == "q4" else family2
+    ld, L = {"q4": family1, "q2": family2, "q3": family3}[fmt]
     spec = ld.spec.with_tokens(T)
     x = synth.gen_x(spec, seed=3)
     xd = gu.x_dev(x, spec.act)
