@@ -75,7 +75,9 @@ def main():
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the verify batch (5 tokens, 2-bit) and the 48-layer 2-bit stack figures")
     ap.add_argument("--stack-steps", type=int, default=20)
-    ap.add_argument("--no-sweep", action="store_true", help="skip the batch sweep T = 8 .. 256")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the batch sweep T = 1 .. 256")
+    ap.add_argument("--no-locality", action="store_true",
+                    help="skip the hot-expert cache-locality figures of the 48-layer stack")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra timing of the same steps replayed from captured HIP graphs")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -241,6 +243,8 @@ def main():
 
     if not args.no_stack:
         extra.update(verify_and_stack(args, dev, q4_layers=layers))
+    if not args.no_locality:
+        extra["hot_expert_locality"] = hot_expert_locality(args, dev)
 
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
@@ -410,6 +414,47 @@ def verify_and_stack(args, dev, q4_layers=None):
         log(f"48-layer stack, T={T}: {us:.1f} us/step ({T / (us * 1e-6):.0f} tok/s), U per layer "
             f"{np.mean(u):.1f}, {100 * out[f'stack48_q2_T{T}_frac_of_8TBps']:.1f} % of 8 TB/s")
         del ws, xs
+    return out
+
+
+def hot_expert_locality(args, dev):
+    """Hot experts kept in the last-level cache (the 256 MB memory-side cache)
+    across decode steps of the 48-layer 2-bit stack: experts numbered by
+    popularity (the Zipf rank of the router bias), the layers' hot_experts set
+    to 0 (every expert streams past the caches), 2, 8 or 512 (every expert
+    cache-allocating), at Zipf exponents 0 (no skew), 1.1 and 2.0; one decode
+    step per timing unit, batch 1 and 8, each step starting from a new token."""
+    import dataclasses
+
+    import torch
+
+    import synth
+    from sparse_moe_router_amd import api, workload
+    from synth import torch_io
+    out = {}
+    stream = torch.cuda.current_stream()
+    for s in (0.0, 1.1, 2.0):
+        base = synth.SPECS["stack_t1"]
+        spec = dataclasses.replace(base, zipf_s=s if s > 0 else None, ordered=True, name=f"stack_zipf{s}")
+        kws = [torch_io.device_filled_kwargs(spec, l, dev) for l in range(spec.n_layers)]
+        for T in (1, 8):
+            xs = torch_io.x_tensor(synth.gen_x(dataclasses.replace(spec, tokens=T), seed=5, tokens=64 * T).storage,
+                                   spec.act, dev)
+            ws = api.workspace(api.Layer(**kws[0]), T, dev)
+            for hot in (0, 2, 8, 512):
+                stack = [api.Layer(**k, hot_experts=hot) for k in kws]
+                bufs = [xs[(i % 64) * T:(i % 64 + 1) * T].clone() for i in range(args.stack_steps + 4)]
+                for k in range(4):
+                    api.moe_stack_forward(stack, bufs[k], T, ws=ws, stream=stream)
+                torch.cuda.synchronize()
+                us = _time_steps(lambda k: api.moe_stack_forward(stack, bufs[4 + k], T, ws=ws, stream=stream),
+                                 args.stack_steps, stream)
+                out[f"zipf{s}_T{T}_hot{hot}_us_per_step"] = us
+                log(f"hot-expert locality: Zipf {s}, T={T}, hot_experts={hot}: {us:.1f} us/step "
+                    f"({T / (us * 1e-6):.0f} tok/s)")
+            del ws
+        del kws
+        torch.cuda.empty_cache()
     return out
 
 

@@ -106,6 +106,17 @@ typedef struct moe_layer {
   const float *router_b; /* [E] fp32 added to the logits, or NULL           */
   moe_experts routed;  /* n == E                                            */
   moe_experts shared;  /* n == 1 (always-active shared expert) or 0 (none)  */
+  int32_t hot_experts; /* >= 0: cache policy of the expert weights (results  */
+                       /* do not depend on it).  The pages keep the most     */
+                       /* used experts resident near the GPU (page 2 "Layer */
+                       /* 1: On-Demand MoE Expert Scheduling"; page 5 "The  */
+                       /* desktop becomes a memory system").  With the       */
+                       /* experts numbered by decreasing popularity, experts */
+                       /* 0 .. hot_experts-1 and the shared expert are read  */
+                       /* with the default (cache-allocating) policy, so     */
+                       /* that they can stay in the last-level cache across  */
+                       /* calls, and the others non-temporally.  0: every    */
+                       /* expert streams (non-temporal).                     */
 } moe_layer;
 
 /* Router + top-K + weights (page 2 "Layer 1": the gating network picks the

@@ -46,7 +46,7 @@ class c_layer(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("qfmt", ctypes.c_int32), ("act", ctypes.c_int32),
                 ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
-                ("routed", c_experts), ("shared", c_experts)]
+                ("routed", c_experts), ("shared", c_experts), ("hot_experts", ctypes.c_int32)]
 
 
 _lib = None
@@ -148,7 +148,7 @@ class Layer:
 
     def __init__(self, *, hidden: int, inter: int, n_experts: int, top_k: int, qfmt, act,
                  router_w: torch.Tensor, router_b: Optional[torch.Tensor], routed: dict,
-                 shared: Optional[dict] = None):
+                 shared: Optional[dict] = None, hot_experts: int = 0):
         self.qfmt = QFMT.get(qfmt, qfmt)
         self.act = ACT.get(act, act)
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
@@ -184,7 +184,7 @@ class Layer:
 
         self.c = c_layer(hidden, inter, n_experts, top_k, self.qfmt, self.act,
                          _ptr(router_w, torch.float32), _ptr(router_b, torch.float32, dev),
-                         ex(routed, n_experts), ex(shared, 1))
+                         ex(routed, n_experts), ex(shared, 1), int(hot_experts))
 
     @property
     def ref(self):

@@ -80,8 +80,9 @@ __device__ __forceinline__ void gateup_rows(const FfnArgs& a, const Work& wk, bo
   };
   load_x(0);
   __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weight loads
-  const MatView vg = expert_view<QF>(shared ? a.sgate : a.gate, shared ? 0 : wk.expert, a.I, a.H);
-  const MatView vu = expert_view<QF>(shared ? a.sup : a.up, shared ? 0 : wk.expert, a.I, a.H);
+  const bool keep = hot_expert(a, shared, wk.expert);
+  const MatView vg = expert_view<QF>(shared ? a.sgate : a.gate, shared ? 0 : wk.expert, a.I, a.H, keep);
+  const MatView vu = expert_view<QF>(shared ? a.sup : a.up, shared ? 0 : wk.expert, a.I, a.H, keep);
   RowTile<QF, RPW, GPL> tg, tu;
   tg.load(vg, rbase, rsub, RPI, a.I, sub, LPR);
   tu.load(vu, rbase, rsub, RPI, a.I, sub, LPR);
@@ -202,8 +203,9 @@ k_gateup1(FfnArgs a) {
   }
   const int rbase = (blockIdx.x * 4 + wave) * RPW;
   RowTile<QF, RPW, 1> tg, tu;
-  tg.load(expert_view<QF>(shared ? a.sgate : a.gate, e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
-  tu.load(expert_view<QF>(shared ? a.sup : a.up, e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+  const bool keep = hot_expert(a, shared, e);
+  tg.load(expert_view<QF>(shared ? a.sgate : a.gate, e, a.I, a.H, keep), rbase, 0, 1, a.I, lane, 64);
+  tu.load(expert_view<QF>(shared ? a.sup : a.up, e, a.I, a.H, keep), rbase, 0, 1, a.I, lane, 64);
   if (wave == 0) put_x1<QF>(xg, lane, xs);
   __syncthreads();
   gateup_rows1<QF, RPW>(a, shared, hrow, rbase, lane, tg, tu, xs);
@@ -248,7 +250,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_s
     };
     load_h(0);
     __builtin_amdgcn_sched_barrier(0);
-    const MatView vd = expert_view<QF>(shared ? a.sdown : a.down, shared ? 0 : wk.expert, a.H, a.I);
+    const MatView vd = expert_view<QF>(shared ? a.sdown : a.down, shared ? 0 : wk.expert, a.H, a.I,
+                                       hot_expert(a, shared, wk.expert));
     RowTile<QF, RPW, GPL> td;
     td.load(vd, rbase, rsub, RPI, a.H, sub, LPR);
     __builtin_amdgcn_sched_barrier(0);
@@ -467,8 +470,9 @@ k_fused_gateup1(RouterArgs r, FfnArgs a) {
   const int rbase = (blockIdx.x * 4 + wave) * RPW;
   RowTile<QF, RPW, 1> tg, tu;
   if (shared) {  // no selection: the weights go out first
-    tg.load(expert_view<QF>(a.sgate, 0, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
-    tu.load(expert_view<QF>(a.sup, 0, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+    const bool keep = hot_expert(a, true, 0);
+    tg.load(expert_view<QF>(a.sgate, 0, a.I, a.H, keep), rbase, 0, 1, a.I, lane, 64);
+    tu.load(expert_view<QF>(a.sup, 0, a.I, a.H, keep), rbase, 0, 1, a.I, lane, 64);
   }
   if (wave == 1) stage_x1<QF>(a.x, a.H, lane, xs);
   if (!shared && wave == 0) {
@@ -493,8 +497,9 @@ k_fused_gateup1(RouterArgs r, FfnArgs a) {
   __syncthreads();
   if (!shared) {
     const int e = __builtin_amdgcn_readfirstlane(s_pick[y]);
-    tg.load(expert_view<QF>(a.gate, e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
-    tu.load(expert_view<QF>(a.up, e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+    const bool keep = hot_expert(a, false, e);
+    tg.load(expert_view<QF>(a.gate, e, a.I, a.H, keep), rbase, 0, 1, a.I, lane, 64);
+    tu.load(expert_view<QF>(a.up, e, a.I, a.H, keep), rbase, 0, 1, a.I, lane, 64);
   }
   gateup_rows1<QF, RPW>(a, shared, shared ? 0 : y, rbase, lane, tg, tu, xs);
 }
@@ -549,7 +554,8 @@ struct Down1Wave {
     const int rsub = lane >> 3, sub = lane & 7;
 #pragma unroll
     for (int js = 0; js < SPW; ++js)
-      tw[js].load(expert_view<QF>(sh[js] ? a.sdown : a.down, e[js], a.H, a.I), rbase, rsub, kDownLpr1, a.H, sub,
+      tw[js].load(expert_view<QF>(sh[js] ? a.sdown : a.down, e[js], a.H, a.I, hot_expert(a, sh[js], e[js])), rbase,
+                  rsub, kDownLpr1, a.H, sub,
                   kDownLpr1);
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {

@@ -66,8 +66,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   for (int k = 0; k < 2; ++k)
     if (wave + 4 * k < nc0) load_x1<QF>(reinterpret_cast<const uint16_t*>(a.x) + (size_t)tok0[k] * a.H, a.H, lane, x0[k]);
   RowTile<QF, RPW, 1> tg, tu;
-  tg.load(expert_view<QF>(shared ? a.sgate : a.gate, shared ? 0 : e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
-  tu.load(expert_view<QF>(shared ? a.sup : a.up, shared ? 0 : e, a.I, a.H), rbase, 0, 1, a.I, lane, 64);
+  const bool keep = hot_expert(a, shared, e);
+  tg.load(expert_view<QF>(shared ? a.sgate : a.gate, shared ? 0 : e, a.I, a.H, keep), rbase, 0, 1, a.I, lane, 64);
+  tu.load(expert_view<QF>(shared ? a.sup : a.up, shared ? 0 : e, a.I, a.H, keep), rbase, 0, 1, a.I, lane, 64);
 #pragma unroll
   for (int k = 0; k < 2; ++k)
     if (wave + 4 * k < nc0) put_x1<QF>(x0[k], lane, xs[wave + 4 * k]);
@@ -140,7 +141,8 @@ __global__ __launch_bounds__(256) void k_down_sb(FfnArgs a, int ny) {
   const bool item0 = it < min(kSbTok, n) * G;
   if (item0) h0.load_raw(hin, (size_t)(lo + it / G) * a.I + (size_t)(it % G) * kGroup);
   RowTile<QF, 1, GPL> tw;
-  tw.load(expert_view<QF>(shared ? a.sdown : a.down, shared ? 0 : e, a.H, a.I), rbase, rsub, kSbLpr, a.H, sub, kSbLpr);
+  tw.load(expert_view<QF>(shared ? a.sdown : a.down, shared ? 0 : e, a.H, a.I, hot_expert(a, shared, e)), rbase,
+          rsub, kSbLpr, a.H, sub, kSbLpr);
   if (item0) put_h(it, h0);
   __syncthreads();
   uint32_t b[GPL][16];

@@ -233,11 +233,21 @@ struct MatView {
   const uint16_t* mins;
   size_t row_bytes;  // code bytes per row
   int groups;        // groups per row
+  bool keep;         // load the codes with the default cache policy (a hot expert), else non-temporally
 };
 
+// Whether an expert's weights are kept in the caches: with hot > 0 the
+// experts numbered below hot (the layer's most popular, when the caller has
+// numbered its experts by popularity) and the shared expert; every other
+// expert streams past the caches.
+__device__ __forceinline__ bool hot_expert(const FfnArgs& a, bool shared, int e) {
+  return a.hot > 0 && (shared || e < a.hot);
+}
+
 template <int QF>
-__device__ __forceinline__ MatView expert_view(const QMat& m, int e, int rows, int cols) {
+__device__ __forceinline__ MatView expert_view(const QMat& m, int e, int rows, int cols, bool keep) {
   MatView v;
+  v.keep = keep;
   v.row_bytes = (size_t)cols * code_bits(QF) / 8;
   v.groups = cols / kGroup;
   v.codes = m.codes + (size_t)e * rows * v.row_bytes;
@@ -261,6 +271,13 @@ struct RowTile {
   // rbase: first row of the wave (uniform); the lane's row is rbase + rsub +
   // rr * rpi.
   __device__ __forceinline__ void load(const MatView& v, int rbase, int rsub, int rpi, int rows, int sub, int lpr) {
+    if (v.keep) load_as<false>(v, rbase, rsub, rpi, rows, sub, lpr);  // uniform branch
+    else load_as<true>(v, rbase, rsub, rpi, rows, sub, lpr);
+  }
+
+  template <bool NT>
+  __device__ __forceinline__ void load_as(const MatView& v, int rbase, int rsub, int rpi, int rows, int sub,
+                                          int lpr) {
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
       const int ru = min(rbase + rr * rpi, rows - 1);          // uniform
@@ -272,7 +289,8 @@ struct RowTile {
         const int gc = min(sub + gi * lpr, v.groups - 1);
         const uint32_t co = (uint32_t)(rc - ru) * (uint32_t)v.row_bytes + (uint32_t)gc * CodeOf<QF>::kBytes;
         const uint32_t so = (uint32_t)(rc - ru) * (uint32_t)v.groups + (uint32_t)gc;
-        c[rr][gi] = __builtin_nontemporal_load(reinterpret_cast<const CT*>(cb + co));
+        if constexpr (NT) c[rr][gi] = __builtin_nontemporal_load(reinterpret_cast<const CT*>(cb + co));
+        else c[rr][gi] = *reinterpret_cast<const CT*>(cb + co);
         s[rr][gi] = sb[so];
         m[rr][gi] = (QF == MOE_Q2_ASYM_G32) ? (v.mins + (size_t)ru * v.groups)[so] : (uint16_t)0;
       }

@@ -13,7 +13,7 @@ using namespace moe;
 
 constexpr int kMaxDim = 4096;
 constexpr int kMaxExperts = 8192;
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -38,7 +38,7 @@ moe_status check_layer(const moe_layer* L) {
   if (L->routed.n != L->n_experts) return MOE_E_ARG;
   if (!qmat_ok(L->routed.gate, L->qfmt) || !qmat_ok(L->routed.up, L->qfmt) || !qmat_ok(L->routed.down, L->qfmt))
     return MOE_E_ARG;
-  if (L->shared.n < 0) return MOE_E_ARG;
+  if (L->shared.n < 0 || L->hot_experts < 0) return MOE_E_ARG;
   if (L->shared.n > 1) return MOE_E_UNSUPPORTED;
   if (L->shared.n == 1 &&
       (!qmat_ok(L->shared.gate, L->qfmt) || !qmat_ok(L->shared.up, L->qfmt) || !qmat_ok(L->shared.down, L->qfmt)))
@@ -118,6 +118,7 @@ FfnArgs ffn_args(const moe_layer& L, const void* x, int32_t T, const int32_t* id
   f.T = T; f.H = L.hidden; f.I = L.inter; f.E = L.n_experts; f.K = L.top_k; f.qfmt = L.qfmt; f.act = L.act;
   f.x = x; f.ids = ids; f.offsets = offsets; f.sorted_pairs = sorted;
   f.h = h; f.hs = f.n_shared ? hs : nullptr; f.o = o; f.so = f.n_shared ? so : nullptr;
+  f.hot = L.hot_experts;
   return f;
 }
 

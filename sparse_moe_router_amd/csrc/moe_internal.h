@@ -82,6 +82,10 @@ struct FfnArgs {
   // matrix-core grouped GEMM, the others on the GEMV kernels.  0: no split
   // (the GEMV kernels take every expert; the grouped GEMM is not launched).
   int mfma_min;
+  // experts numbered below hot (and the shared expert) are loaded with the
+  // default cache policy so that they stay in the caches across calls; 0: every
+  // expert streams past them (non-temporal loads)
+  int hot;
 };
 // the GEMV kernels skip an expert with n tokens that the grouped GEMM takes
 __host__ __device__ inline bool on_mfma(const FfnArgs& a, int n) { return a.mfma_min > 0 && n >= a.mfma_min; }

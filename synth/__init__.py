@@ -57,6 +57,7 @@ class LayerSpec:
     n_shared: int = 1
     n_layers: int = 1
     weight_std: float = 0.02
+    ordered: bool = False         # experts numbered by decreasing popularity (Zipf rank e + 1)
 
     def with_tokens(self, t: int) -> "LayerSpec":
         return replace(self, tokens=t)
@@ -278,8 +279,12 @@ def gen_router(spec: LayerSpec, seed: int = 0, layer: int = 0):
     if spec.zipf_s is None:
         return w, None
     # Zipf(s) prior over a random ranking of the experts, as a logit offset:
-    # b_e = -s * ln(rank_e) with ranks 1..E (the normaliser cancels in top-k and softmax).
-    ranks = 1 + rng(seed, spec.family, layer, _T_ROUTER_RANK).permutation(spec.n_experts)
+    # b_e = -s * ln(rank_e) with ranks 1..E (the normaliser cancels in top-k and softmax);
+    # with spec.ordered the experts are numbered by popularity (rank_e = e + 1)
+    if spec.ordered:
+        ranks = 1 + np.arange(spec.n_experts)
+    else:
+        ranks = 1 + rng(seed, spec.family, layer, _T_ROUTER_RANK).permutation(spec.n_experts)
     b = (-spec.zipf_s * np.log(ranks.astype(np.float64))).astype(np.float32)
     return w, b
 

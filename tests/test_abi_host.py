@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert api.moe_abi_version() == 2
+    assert api.moe_abi_version() == 3
     for s in range(5):
         assert api.lib().moe_status_str(s).startswith(b"MOE_")
 
@@ -82,6 +82,14 @@ def test_q2_requires_mins():
     assert ws_bytes(L, 1) > 0
     L.routed.down.mins = None
     assert ws_bytes(L, 1) == 0
+
+
+def test_negative_hot_experts_rejected():
+    L = layer()
+    L.hot_experts = -1
+    assert ws_bytes(L, 1) == 0
+    L.hot_experts = 10**6  # any count from 0 up is valid
+    assert ws_bytes(L, 1) > 0
 
 
 def test_q3_format_accepted_without_mins():

@@ -12,6 +12,7 @@ import torch
 import synth
 from oracle import moe_oracle as mo
 from sparse_moe_router_amd import api
+from synth import torch_io
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
@@ -342,6 +343,25 @@ def test_power_of_two_down_scales_double_y_bitwise(qfmt):
     a = gu.run_forward(gu.device_layer(ld), xd, 5)
     b = gu.run_forward(gu.device_layer(_doubled(ld)), xd, 5)
     assert np.array_equal(b["y"], 2 * a["y"])
+
+
+@pytest.mark.parametrize("T", [1, 5, 40])
+def test_hot_expert_policy_keeps_the_bits(T):
+    """hot_experts (the cache policy of the experts' weight loads) leaves every
+    result bit unchanged, on popularity-numbered experts: one token (fused
+    kernels), a small batch and the per-expert GEMV (I not a multiple of 128)."""
+    spec = synth.LayerSpec("hot", 2048, 64, 10, 96 if T == 40 else 768, T, "q4_sym_g32", "bf16", 0.0221, 1.1,
+                           family=75, ordered=True)
+    ld = synth.gen_layer(spec)
+    kw = torch_io.layer_kwargs(ld, gu.DEV)
+    xd = gu.x_dev(synth.gen_x(spec), spec.act)
+    outs = []
+    for hot in (0, 4, 64):
+        f = gu.run_forward(api.Layer(**kw, hot_experts=hot), xd, T, x_next=True)
+        outs.append(f)
+    for f in outs[1:]:
+        assert np.array_equal(f["y"], outs[0]["y"]) and np.array_equal(f["ids"], outs[0]["ids"])
+        assert torch.equal(f["x_next"].view(torch.int16), outs[0]["x_next"].view(torch.int16))
 
 
 def test_reruns_are_bitwise_identical():
