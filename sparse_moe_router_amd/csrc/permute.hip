@@ -90,7 +90,20 @@ __global__ __launch_bounds__(64) void k_perm_small(PermuteArgs a) {
   const int n = a.T * a.K, E = a.E;
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
   __syncthreads();
-  for (int p = lane; p < n; p += 64) atomicAdd(&cnt[a.ids[p]], 1);
+  // the ids of 16 rounds are requested together before their counts are
+  // added (a load per round, waiting for each, costs a memory latency each)
+  constexpr int kRounds = 16;
+  for (int p0 = 0; p0 < n; p0 += 64 * kRounds) {
+    int ev[kRounds];
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int p = p0 + 64 * i + lane;
+      ev[i] = p < n ? a.ids[p] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i)
+      if (ev[i] >= 0) atomicAdd(&cnt[ev[i]], 1);
+  }
   __syncthreads();
   // lane owns experts [lane*per, (lane+1)*per)
   const int per = (E + 63) / 64;
