@@ -6,8 +6,8 @@ through a 512-expert top-10 + 1 shared layer (H 2048, I 768, 4-bit group-32
 weights, bf16 activations), with the inputs resident in HBM.  Consecutive
 steps rotate over 16 distinct copies of the layer's weights (21.8 GB) so the
 experts stream from HBM and not from the 256 MB last-level cache.  The K timed
-steps are replayed from captured HIP graphs (16 steps per graph); the same
-steps launched directly are reported beside them.
+steps are replayed from captured HIP graphs (up to 256 steps per graph); the
+same steps launched directly are reported beside them.
 
 Prints one JSON line (rank 0, N = 1):
   value        decode tokens/s (whole job)
@@ -45,7 +45,8 @@ PEAK_HBM_GBS = 8000.0
 # sources whose fingerprint is stored; reported as null once they change.
 TRAFFIC_SOURCES = ("router.hip", "expert_gemv.hip", "gemv_one.h", "gemv_tile.h", "moe_device.h", "topk.h",
                    "moe_internal.h", "moe_abi.cpp")
-MEASURED_TRAFFIC = {"bytes_per_step": None, "sources_sha256": ""}
+MEASURED_TRAFFIC = {"bytes_per_step": 33959726,
+                    "sources_sha256": "62f7580774a00d99ceae3bf559f49e78c64215079edb84c9b7f7c0c407a3c5b4"}
 
 
 def kernel_sources_sha256() -> str:
@@ -71,7 +72,6 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 4096-token prefill figure")
     ap.add_argument("--prefill-steps", type=int, default=16)
-    ap.add_argument("--kernel-reps", type=int, default=2000)
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the verify batch (5 tokens, 2-bit) and the 48-layer 2-bit stack figures")
     ap.add_argument("--stack-steps", type=int, default=20)
@@ -153,14 +153,15 @@ def main():
     log(f"decode, direct launches: {direct_us:.2f} us/step")
 
     # the timed steps replayed from captured HIP graphs (a serving loop's way of
-    # launching a step): graphs of up to 16 consecutive steps, the K timed
-    # steps covered exactly, the same (copy, token) sequence as above
+    # launching a step): graphs of up to 256 consecutive steps (one graph for
+    # K <= 256), the K timed steps covered exactly, the same (copy, token)
+    # sequence as above
     graph_us = None
     decode_launch = "direct"
     ms_per_step = direct_us * 1e-3
     if not args.no_graph:
         cap = torch.cuda.Stream()
-        g_len = 16
+        g_len = 256
 
         def capture(first, n):
             g = torch.cuda.CUDAGraph()
@@ -180,7 +181,7 @@ def main():
         torch.cuda.synchronize()
         graph_us = start.elapsed_time(end) * 1e3 / args.steps
         log(f"decode, HIP graph replay: {graph_us:.2f} us/step")
-        decode_launch = "HIP graph replay (graphs of 16 steps)"
+        decode_launch = f"HIP graph replay ({len(graphs)} graph{'s' if len(graphs) > 1 else ''} of up to {g_len} steps)"
         ms_per_step = graph_us * 1e-3
     tok_s = 1e3 / ms_per_step
     log(f"decode: {ms_per_step * 1e3:.2f} us/step, {tok_s:.0f} tok/s ({decode_launch})")
