@@ -8,9 +8,8 @@
 // position; then it owns all of the expert's tokens (sorted positions y ..
 // y + n - 1); the last block row is the shared expert (all T tokens).  The
 // expert's weight rows are loaded once; the tokens' activations are staged in
-// LDS, prepared, chunk by chunk.  gate/up keeps its codes packed in registers
-// and unpacks them again for every token (unpacked, they would cost two waves
-// per SIMD of occupancy); down unpacks its codes once for all the tokens.
+// LDS, prepared, chunk by chunk.  Both kernels unpack the codes once for all
+// the tokens.
 #include "gemv_one.h"
 
 namespace moe {
@@ -74,17 +73,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     if (wave + 4 * k < nc0) put_x1<QF>(x0[k], lane, xs[wave + 4 * k]);
   __syncthreads();
   const bool gok = lane < a.H / kGroup;
+  // the codes are unpacked once for all the expert's tokens (the block keeps
+  // four waves per SIMD with them unpacked)
   uint32_t bg[RPW][16], bu[RPW][16];
-  // 3-bit codes take four instructions per pair to unpack (4-bit and 2-bit:
-  // one or two), so they are unpacked once for all the tokens; the other
-  // formats unpack again per token and keep more waves per SIMD
-  constexpr bool kUnpackOnce = QF == MOE_Q3_SYM_G32;
-  if constexpr (kUnpackOnce) {
 #pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      unpack_group<QF>(tg.c[rr][0], bg[rr]);
-      unpack_group<QF>(tu.c[rr][0], bu[rr]);
-    }
+  for (int rr = 0; rr < RPW; ++rr) {
+    unpack_group<QF>(tg.c[rr][0], bg[rr]);
+    unpack_group<QF>(tu.c[rr][0], bu[rr]);
   }
   void* out = shared ? a.hs : a.h;
   for (int c0 = 0; c0 < n; c0 += kSbTok) {
@@ -102,9 +97,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
       for (int rr = 0; rr < RPW; ++rr) {
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (!kUnpackOnce) unpack_group<QF>(tg.c[rr][0], bg[rr]);
         const float gv = group_acc_unpacked<QF>(0.f, bg[rr], tg.s[rr][0], tg.m[rr][0], xg);
-        if constexpr (!kUnpackOnce) unpack_group<QF>(tu.c[rr][0], bu[rr]);
         const float uv = group_acc_unpacked<QF>(0.f, bu[rr], tu.s[rr][0], tu.m[rr][0], xg);
         v[rr] = gok ? gv : 0.f;
         v[RPW + rr] = gok ? uv : 0.f;
