@@ -83,12 +83,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 // so with bf16 x every product x * part is exact in fp32 and the MFMA chain
 // lo, mid, hi accumulates sum_k x_k w_k in fp32 like any fp32 dot product,
 // over 3 H exact terms.  The split is done in registers per 32-k step.
-// Block: 64 tokens x 64 experts, 4 waves; wave w owns experts n0 + 16 w ..
-// + 15 and all 64 tokens (4 MFMA tiles of 16 x 16); the x tile is staged
-// through LDS in 128-k chunks (double buffered), shared by the 4 waves.
+//
+// The operands reach LDS by the DMA path (global_load_lds: lane i of an
+// instruction lands at the wave-uniform LDS base + 16 i) in chunks of 64 k,
+// each instruction reading whole 64-byte runs of a row per four lanes (a quad
+// of lanes reading four different rows costs the address unit four times as
+// many requests).  Within a chunk the MFMA steps s = 0, 1 take, in lane
+// group c, the k = 16 c + 8 s + e (e < 8): a permutation of the chunk's k,
+// the same for x and W, so the dot products are unchanged.  Layouts, with
+// every DMA instruction's kilobyte at a 1040-byte stride (16 bytes of skew):
+//   x: instruction j < 8 holds rows j + 8 m (m < 8), 128 bytes each;
+//   W: instruction 4 nt + j holds rows 16 nt + j + 4 m (m < 4), 256 bytes
+//      each, rotated by 4 m 16-byte units,
+// so that the 16 lanes of a read phase hit 16 distinct bank groups.
+// Two tilings (64 tokens by 16 NT experts per block, 4 waves):
+//   split over k (NT = 1, fewer than 1024 tokens): each wave streams a
+//     quarter of the chunks through its own LDS ring, and the 4 partial
+//     tiles are added in LDS in wave order (a fixed order);
+//   split over experts (NT = 4): the waves share one ring, wave w owns the
+//     16 experts of tile w.
+// Workgroups are dealt round-robin over the 8 XCDs, so the blocks are
+// numbered such that those of one token tile share an XCD (and its L2 copy of
+// the x tile).  H must be a multiple of 64 (else the fp32 router runs).
 constexpr int kRouterMfmaMinTokens = 128;
-constexpr int kRM = 64, kRN = 64, kRKC = 128;
-constexpr int kRRow = kRKC + 8;  // bf16 per LDS row (+8: conflict-free 16-byte reads)
+constexpr int kRouterWideTokens = 1024;  // from here on: split over experts
+constexpr int kRChunkK = 64;             // k per chunk
+constexpr int kRInst = 1040;             // LDS bytes per DMA instruction (1 KiB + skew)
 
 typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float rf32x4_t __attribute__((ext_vector_type(4)));
@@ -112,98 +132,161 @@ __device__ __forceinline__ void split3(float w0, float w1, uint32_t& hi, uint32_
   lo = __builtin_amdgcn_perm(l1, l0, 0x07060302u);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_router_mfma(RouterArgs a) {
-  __shared__ __align__(16) uint16_t s_x[2][kRM * kRRow];
-  const int m0 = blockIdx.x * kRM, n0 = blockIdx.y * kRN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int NT, bool SPLITK, int RING>
+__global__ __launch_bounds__(256) void k_router_mfma(RouterArgs a, int nblocks, int per_xcd) {
+  constexpr int XI = 8, WI = 4 * NT;                    // DMA instructions per chunk: x, W
+  constexpr int CHUNK = (XI + WI) * kRInst;             // bytes of one ring slot
+  constexpr int RINGS = SPLITK ? 4 : 1;                 // one ring per wave, or one per block
+  constexpr int INST_W = SPLITK ? XI + WI : (XI + WI) / 4;  // DMA instructions per wave per chunk
+  __shared__ __align__(16) uint8_t s_ring[RINGS * RING * CHUNK];
+  const int bl = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int mblocks = (a.T + 63) / 64;
+  if (bl >= mblocks * nblocks) return;  // whole block: before any barrier
+  const int m0 = (bl / nblocks) * 64, n0 = (bl % nblocks) * 16 * NT;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, lc = lane >> 4;
-  const int nchunks = (a.H + kRKC - 1) / kRKC;
+  const int nchunks = a.H / kRChunkK;
+  int c0 = 0, c1 = nchunks;
+  if constexpr (SPLITK) {
+    const int per = (nchunks + 3) / 4;
+    c0 = min(wave * per, nchunks);
+    c1 = min(c0 + per, nchunks);  // c0 == c1: this wave adds zeros
+  }
+  uint8_t* ring = s_ring + (SPLITK ? wave * RING * CHUNK : 0);
 
-  // staging: thread -> token row r = tid / 4, 32-k slice q = tid % 4 of the chunk (4 x 16 bytes)
-  const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
-  const uint16_t* xrow = reinterpret_cast<const uint16_t*>(a.x) + (size_t)min(m0 + r, a.T - 1) * a.H;
-  ru32x4_t st[4];  // native vectors: with HIP's uint4 the compiler kept this array in scratch memory
-  auto load_x = [&](int kc) {
-    const int k = min(kc * kRKC + q * 32, a.H - 32);  // past H: any in-range slice, never used
-    const ru32x4_t* src = reinterpret_cast<const ru32x4_t*>(xrow + k);
+  // this lane's source of each of the wave's DMA instructions (byte offset of
+  // chunk 0; chunk c adds 128 c for x, 256 c for W) and its destination
+  // instruction index within a ring slot.  Rows past T or E read the last row;
+  // their results are dropped.
+  const uint8_t* src[INST_W];
+  int cstride[INST_W], dst[INST_W];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st[i] = src[i];
-  };
-  auto store_x = [&](int buf) {
-    ru32x4_t* dst = reinterpret_cast<ru32x4_t*>(&s_x[buf][r * kRRow + q * 32]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = st[i];
-  };
-
-  // B: this lane's expert row and k offset within a 32-k step
-  const int e = min(n0 + wave * 16 + ln, a.E - 1);
-  const float* wrow = a.w + (size_t)e * a.H + lc * 8;
-  rf32x4_t acc[4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) acc[mt] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // this lane's 8 weights of each 32-k step of a chunk, prefetched one chunk ahead
-  float4 wv[4][2], wn[4][2];
-  auto load_w = [&](int kc, float4 (&w)[4][2]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = min(kc * kRKC + j * 32, a.H - 32);  // past H: any in-range step, never used
-      w[j][0] = *reinterpret_cast<const float4*>(wrow + k);
-      w[j][1] = *reinterpret_cast<const float4*>(wrow + k + 4);
+  for (int i = 0; i < INST_W; ++i) {
+    const int J = SPLITK ? i : wave * INST_W + i;  // instruction of the chunk
+    dst[i] = J;
+    if (J < XI) {  // x: row j + 8 m, unit lane % 8
+      const int m = lane >> 3, row = min(m0 + J + 8 * m, a.T - 1);
+      src[i] = reinterpret_cast<const uint8_t*>(a.x) + (size_t)row * a.H * 2 + (lane & 7) * 16;
+      cstride[i] = kRChunkK * 2;
+    } else {  // W: tile nt, row 16 nt + j + 4 m, unit (p - 4 m) mod 16 at position p
+      const int jw = J - XI, nt = jw >> 2, j = jw & 3, m = lane >> 4, p = lane & 15;
+      const int row = min(n0 + 16 * nt + j + 4 * m, a.E - 1);
+      src[i] = reinterpret_cast<const uint8_t*>(a.w) + (size_t)row * a.H * 4 + ((p - 4 * m) & 15) * 16;
+      cstride[i] = kRChunkK * 4;
     }
+  }
+  auto issue = [&](int c, int slot) {  // chunk c (clamped: past the end, a slot that is never read)
+    const int cc = min(c, c1 - 1);
+#pragma unroll
+    for (int i = 0; i < INST_W; ++i)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + (size_t)cc * cstride[i]),
+                                       static_cast<void*>(ring + slot * CHUNK + dst[i] * kRInst), 16, 0, 0);
   };
 
-  load_x(0);
-  load_w(0, wv);
-  store_x(0);
-  __syncthreads();
-  for (int kc = 0; kc < nchunks; ++kc) {
-    const int buf = kc & 1;
-    const int steps = min(kRKC, a.H - kc * kRKC) / 32;  // H is a multiple of 32
-    // the next chunk's loads and LDS store are branch-free (indices clamped;
-    // after the last chunk they fill a buffer that is never read), so the
-    // staged values stay in registers and no wait lands before the products
-    load_x(kc + 1);
-    load_w(kc + 1, wn);
+  // read addresses (within a slot) of the MFMA operands of step s:
+  //   A, tile mt: row R = 16 mt + ln -> instruction R % 8, offset 128 (R / 8) + 16 (2 lc + s)
+  //   B, tile nt, half h: row n = ln -> instruction 8 + 4 nt + n % 4,
+  //      offset 256 (n / 4) + 16 ((4 lc + 2 s + h + 4 (n / 4)) mod 16)
+  constexpr int NTW = SPLITK ? NT : 1;  // N tiles this wave computes
+  const int nt0 = SPLITK ? 0 : wave;
+  int aoff[4], boff[NTW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < steps) {
+  for (int mt = 0; mt < 4; ++mt) {
+    const int R = 16 * mt + ln;
+    aoff[mt] = (R & 7) * kRInst + (R >> 3) * 128 + 32 * lc;
+  }
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) boff[t] = (XI + 4 * (nt0 + t) + (ln & 3)) * kRInst + (ln >> 2) * 256;
+  const int brot = 4 * lc + 4 * (ln >> 2);  // unit of (s, h) = (0, 0) before the mod
+
+  rf32x4_t acc[4][NTW];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acc[mt][t] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int slot) {
+    const uint8_t* base = ring + slot * CHUNK;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      ru32x4_t xa[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) xa[mt] = *reinterpret_cast<const ru32x4_t*>(base + aoff[mt] + 16 * s);
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const rf32x4_t w0 = *reinterpret_cast<const rf32x4_t*>(base + boff[t] + 16 * ((brot + 2 * s) & 15));
+        const rf32x4_t w1 = *reinterpret_cast<const rf32x4_t*>(base + boff[t] + 16 * ((brot + 2 * s + 1) & 15));
         uint32_t h[4], m[4], l[4];
-        split3(wv[j][0].x, wv[j][0].y, h[0], m[0], l[0]);
-        split3(wv[j][0].z, wv[j][0].w, h[1], m[1], l[1]);
-        split3(wv[j][1].x, wv[j][1].y, h[2], m[2], l[2]);
-        split3(wv[j][1].z, wv[j][1].w, h[3], m[3], l[3]);
+        split3(w0[0], w0[1], h[0], m[0], l[0]);
+        split3(w0[2], w0[3], h[1], m[1], l[1]);
+        split3(w1[0], w1[1], h[2], m[2], l[2]);
+        split3(w1[2], w1[3], h[3], m[3], l[3]);
         const ru32x4_t hi = {h[0], h[1], h[2], h[3]}, mid = {m[0], m[1], m[2], m[3]}, lo = {l[0], l[1], l[2], l[3]};
+        // each tile takes lo, mid, hi in that order; the 4 tiles interleave
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const ru32x4_t xa = *reinterpret_cast<const ru32x4_t*>(&s_x[buf][(mt * 16 + ln) * kRRow + j * 32 + lc * 8]);
-          acc[mt] = router_mfma(xa, lo, acc[mt]);
-          acc[mt] = router_mfma(xa, mid, acc[mt]);
-          acc[mt] = router_mfma(xa, hi, acc[mt]);
-        }
+        for (int mt = 0; mt < 4; ++mt) acc[mt][t] = router_mfma(xa[mt], lo, acc[mt][t]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt][t] = router_mfma(xa[mt], mid, acc[mt][t]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt][t] = router_mfma(xa[mt], hi, acc[mt][t]);
       }
     }
-    store_x(buf ^ 1);
+  };
+
+  // the DMA writes LDS behind the compiler's back: its completion is awaited
+  // with vmcnt (the wave's DMA instructions complete in order; the loop
+  // issues no other vector-memory load), with a memory clobber
+  if (c0 < c1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      wv[j][0] = wn[j][0];
-      wv[j][1] = wn[j][1];
+    for (int r = 0; r < RING - 1; ++r) issue(c0 + r, r);
+    for (int c = c0; c < c1; ++c) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INST_W * (RING - 2)) : "memory");
+      if constexpr (!SPLITK) __syncthreads();  // every wave's part of chunk c is in; chunk c - 1 is done
+      __builtin_amdgcn_sched_barrier(0);
+      issue(c + RING - 1, (c - c0 + RING - 1) % RING);
+      compute((c - c0) % RING);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped tail loads land before the ring is reused
+
+  if constexpr (SPLITK) {
+    // partial tiles of waves 1..3 -> LDS (the ring's first bytes), added by wave 0 in wave order
+    rf32x4_t* part = reinterpret_cast<rf32x4_t*>(s_ring);
+    __syncthreads();
+    if (wave > 0) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) part[((wave - 1) * 4 + mt) * 64 + lane] = acc[mt][0];
     }
     __syncthreads();
+    if (wave > 0) return;
+    for (int w = 1; w < 4; ++w)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][0] += part[((w - 1) * 4 + mt) * 64 + lane];
   }
 
-  // D lane l holds tokens 4 (l / 16) + i of each M tile, expert ln of the wave's 16
-  const int en = n0 + wave * 16 + ln;
-  if (en < a.E) {
+  // D lane l holds tokens 4 (l / 16) + i of each M tile, expert l % 16 of the N tile
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int en = n0 + 16 * (nt0 + t) + ln;
+    if (en >= a.E) continue;
     const float bias = a.b ? a.b[en] : 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = m0 + mt * 16 + lc * 4 + i;
-        if (t < a.T) a.logits[(size_t)t * a.E + en] = acc[mt][i] + bias;
+        const int tk = m0 + mt * 16 + lc * 4 + i;
+        if (tk < a.T) a.logits[(size_t)tk * a.E + en] = acc[mt][t][i] + bias;
       }
   }
+}
+
+template <int NT, bool SPLITK, int RING>
+static void router_mfma(const RouterArgs& a, hipStream_t s) {
+  const int nblocks = (a.E + 16 * NT - 1) / (16 * NT);
+  const int total = (a.T + 63) / 64 * nblocks;
+  const int per_xcd = (total + 7) / 8;
+  k_router_mfma<NT, SPLITK, RING><<<dim3(8 * per_xcd), dim3(256), 0, s>>>(a, nblocks, per_xcd);
 }
 
 // One wave per token, E <= 1024 (logits in registers).
@@ -325,8 +408,11 @@ static void router_nch(const RouterArgs& a, dim3 grid, hipStream_t s) {
 
 hipError_t launch_router_logits(const RouterArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (a.act == MOE_ACT_BF16 && a.T >= kRouterMfmaMinTokens) {
-    k_router_mfma<<<dim3((a.T + kRM - 1) / kRM, (a.E + kRN - 1) / kRN), 256, 0, s>>>(a);
+  if (a.act == MOE_ACT_BF16 && a.T >= kRouterMfmaMinTokens && a.H % kRChunkK == 0) {
+    // rings of two chunks: a third slot measured no faster (the loop is bound
+    // by its split and MFMA work, not by the DMA's latency)
+    if (a.T >= kRouterWideTokens) router_mfma<4, false, 2>(a, s);
+    else router_mfma<1, true, 2>(a, s);
     return hipGetLastError();
   }
   const int chunks = (a.T + 3) / 4;

@@ -75,8 +75,9 @@ ROUTER_MFMA_MIN_TOKENS = 128
 
 def router_parts(spec, T):
     """Parts per weight of the library's logit evaluation for a call of T tokens:
-    3 on the matrix-core path (bf16 x, T >= 128), else 1 (an fp32 dot product)."""
-    return 3 if spec.act == synth.ACT_BF16 and T >= ROUTER_MFMA_MIN_TOKENS else 1
+    3 on the matrix-core path (bf16 x, T >= 128, H a multiple of 64), else 1
+    (an fp32 dot product)."""
+    return 3 if spec.act == synth.ACT_BF16 and T >= ROUTER_MFMA_MIN_TOKENS and spec.hidden % 64 == 0 else 1
 
 
 def check_routing(ld: synth.LayerData, xv: np.ndarray, gpu: dict, tokens=None):

@@ -142,7 +142,8 @@ TIE_CASES = [
     ("fused_few_tokens_k20", 512, 20, 1, "forward"),  # k_fused_gateup (K > 16)
     ("route_small", 512, 10, 5, "forward"),           # k_route_small (T K <= 256)
     ("topk_regs_fp32_router", 512, 10, 3, "router"),  # k_router_logits + k_topk_regs
-    ("topk_regs_mfma_router", 512, 10, 130, "router"),  # k_router_mfma + k_topk_regs
+    ("topk_regs_mfma_router", 512, 10, 130, "router"),  # k_router_mfma split over k + k_topk_regs
+    ("topk_regs_mfma_wide_router", 512, 10, 1030, "router"),  # k_router_mfma split over experts
     ("topk_lds", 1500, 10, 4, "router"),              # E > 1024: k_topk_lds
 ]
 

@@ -212,13 +212,17 @@ def test_many_tokens_per_expert(case):
     full_check(ld, x, strict=i >= 768)
 
 
-@pytest.mark.parametrize("shape", [(96, 70, 5, 130), (2048, 512, 10, 257), (4096, 64, 3, 140), (160, 1500, 7, 129),
+@pytest.mark.parametrize("shape", [(2048, 512, 10, 257), (4096, 64, 3, 140), (192, 1500, 7, 129), (64, 40, 3, 200),
+                                   (128, 70, 5, 1100), (2048, 512, 10, 1024), (96, 70, 5, 130), (160, 1500, 7, 129),
                                    (2048, 512, 10, 40), (160, 1500, 7, 65)],
                          ids=lambda c: "H{}_E{}_K{}_T{}".format(*c))
 def test_router_many_tokens(shape):
     """Router logits for many tokens: on the matrix cores from 128 bf16 tokens
-    (ragged token and expert tiles, H not a multiple of the 128-wide staging
-    chunk, E > 1024), and the multi-token fp32 pass below that."""
+    when H is a multiple of the 64-wide chunk -- split over k below 1024
+    tokens (ragged token and expert tiles, E > 1024, H of 3 chunks and of 1
+    chunk, so that some waves have no chunk), split over experts from 1024
+    (ragged 64-expert tile) -- and the fp32 pass otherwise (H = 96, 160) and
+    below 128 tokens."""
     h, e, k, t = shape
     spec = synth.LayerSpec("router", h, e, k, 64, t, "q4_sym_g32", "bf16", h ** -0.5, 1.1, family=72 + h + e)
     ld = synth.gen_layer(spec, routed_ids=[0])
