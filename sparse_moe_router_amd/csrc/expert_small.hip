@@ -21,10 +21,18 @@ constexpr int kSbMaxPairs = 256;  // T K of the small-batch path (one block row 
 
 // The expert of block row y: first sorted position lo and token count n, or
 // false when y is not the first position of its expert.  Shared row: y == ny.
+// With the routing's work list, block row y takes its u = y-th distinct
+// expert instead (one load, and the rows past the last expert exit at once).
 __device__ __forceinline__ bool sb_work(const FfnArgs& a, int ny, int y, int* expert, int* lo, int* n) {
   if (y == ny) {
     *expert = -1; *lo = 0; *n = a.T;
     return !on_mfma(a, a.T);
+  }
+  if (a.work) {
+    const int4 w = reinterpret_cast<const int4*>(a.work)[y];
+    if (w.x < 0) return false;
+    *expert = w.x; *lo = w.y; *n = w.z;
+    return !on_mfma(a, w.z);
   }
   const int p = a.sorted_pairs[y];
   const int pp = y > 0 ? a.sorted_pairs[y - 1] : p;
@@ -36,7 +44,7 @@ __device__ __forceinline__ bool sb_work(const FfnArgs& a, int ny, int y, int* ex
 
 // token of the expert's jj-th sorted position
 __device__ __forceinline__ int sb_token(const FfnArgs& a, bool shared, int lo, int jj) {
-  return shared ? jj : a.sorted_pairs[lo + jj] / a.K;
+  return shared ? jj : a.sorted_tok ? a.sorted_tok[lo + jj] : a.sorted_pairs[lo + jj] / a.K;
 }
 
 // gate/up + SwiGLU: wave w owns rows (blockIdx.x * 4 + w) * RPW .. + RPW - 1
@@ -49,13 +57,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int y = blockIdx.y;
   // tokens of the first chunk's positions y + wave and y + wave + 4, read
-  // with the expert lookup (clamped in range; used only below the count)
+  // with the expert lookup (clamped in range; used only below the count);
+  // with a work list, from the expert's first position once it is known
   int tok0[2];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) tok0[k] = y == ny ? wave + 4 * k : a.sorted_pairs[min(y + wave + 4 * k, ny - 1)] / a.K;
+  for (int k = 0; k < 2; ++k)
+    tok0[k] = y == ny || a.work ? wave + 4 * k : a.sorted_pairs[min(y + wave + 4 * k, ny - 1)] / a.K;
   int e, lo, n;
   if (!sb_work(a, ny, y, &e, &lo, &n)) return;
   const bool shared = e < 0;
+  if (a.work && !shared) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) tok0[k] = a.sorted_tok[lo + min(wave + 4 * k, n - 1)];
+  }
   const int rbase = (blockIdx.x * 4 + wave) * RPW;
   // the first chunk's activations go out before the weight rows: loads
   // complete in order, so they are staged while the weights are in flight

@@ -56,7 +56,7 @@ moe_status check_tokens(const moe_layer* L, int32_t T) {
 
 // Workspace regions (byte offsets), each 256-byte aligned.
 struct Ws {
-  size_t logits, ids, w, offsets, sorted, pos, chunk, h, hs, o, so, y, total;
+  size_t logits, ids, w, offsets, sorted, pos, chunk, work, stok, h, hs, o, so, y, total;
 };
 
 Ws ws_layout(const moe_layer& L, int32_t T) {
@@ -76,6 +76,8 @@ Ws ws_layout(const moe_layer& L, int32_t T) {
   w.sorted = take(t * k * 4);
   w.pos = take(t * k * 4);
   w.chunk = take(permute_scratch_ints(T, L.top_k, L.n_experts) * 4);
+  w.work = take(t * k * 16);
+  w.stok = take(t * k * 4);
   w.h = take(t * k * L.inter * a);
   w.hs = take(t * L.inter * a);
   w.o = take(t * k * L.hidden * 4);
@@ -130,8 +132,8 @@ moe_status layer_forward_impl(const moe_layer& L, const void* x, int32_t T, floa
   const RouterArgs ra = router_args(L, x, T, at<float>(ws, W.logits), ids, wts);
   PermuteArgs pa{ids, at<int32_t>(ws, W.offsets), at<int32_t>(ws, W.sorted), at<int32_t>(ws, W.pos),
                  at<int32_t>(ws, W.chunk), T, L.top_k, L.n_experts};
-  const FfnArgs fa = ffn_args(L, x, T, ids, pa.offsets, pa.sorted_pairs, at<void>(ws, W.h), at<void>(ws, W.hs),
-                              at<float>(ws, W.o), at<float>(ws, W.so));
+  FfnArgs fa = ffn_args(L, x, T, ids, pa.offsets, pa.sorted_pairs, at<void>(ws, W.h), at<void>(ws, W.hs),
+                        at<float>(ws, W.o), at<float>(ws, W.so));
   const CombineArgs ca{fa.o, fa.so, pa.pair_pos, wts, x_next ? x : nullptr, x_next, y, T, L.hidden, L.top_k, L.act};
   MOE_TRY(dev(launch_router_logits(ra, s)));
   if (fused_decode_ok(T, L.top_k, L.n_experts, L.hidden, L.inter, L.act)) {
@@ -142,6 +144,11 @@ moe_status layer_forward_impl(const moe_layer& L, const void* x, int32_t T, floa
     return dev(launch_combine(ca, s));
   }
   if (route_small_ok(T, L.top_k, L.n_experts)) {
+    // with the work list: the small-batch kernels find their expert in one load
+    pa.work = at<int32_t>(ws, W.work);
+    pa.sorted_tok = at<int32_t>(ws, W.stok);
+    fa.work = pa.work;
+    fa.sorted_tok = pa.sorted_tok;
     MOE_TRY(dev(launch_route_small(ra, pa, s)));
   } else {
     MOE_TRY(dev(launch_topk(ra, s)));

@@ -56,6 +56,12 @@ struct PermuteArgs {
   int32_t* pair_pos;
   int32_t* chunk_base;  // [n_chunks][E] scratch
   int T, K, E;
+  // written by the small-batch routing only (else null): work[u] = (expert,
+  // first sorted position, token count, 0) of the u-th distinct expert in
+  // sorted order and (-1, 0, 0, 0) past the last, for u < T K; sorted_tok[y]
+  // = the token of sorted position y
+  int32_t* work = nullptr;
+  int32_t* sorted_tok = nullptr;
 };
 size_t permute_scratch_ints(int T, int K, int E);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
@@ -86,6 +92,11 @@ struct FfnArgs {
   // default cache policy so that they stay in the caches across calls; 0: every
   // expert streams past them (non-temporal loads)
   int hot;
+  // the small-batch routing's work list and tokens by sorted position
+  // (PermuteArgs), or null: the small-batch kernels then find their expert
+  // from ids, sorted_pairs and offsets
+  const int32_t* work = nullptr;
+  const int32_t* sorted_tok = nullptr;
 };
 // the GEMV kernels skip an expert with n tokens that the grouped GEMM takes
 __host__ __device__ inline bool on_mfma(const FfnArgs& a, int n) { return a.mfma_min > 0 && n >= a.mfma_min; }

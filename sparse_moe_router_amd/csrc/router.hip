@@ -340,9 +340,14 @@ __device__ __forceinline__ const float* lg_row(const RouterArgs& a, int t) { ret
 // #{q : (e_q, q) < (e_p, p)}; offsets[e] is the first rank with expert >= e.
 template <int PL, int NWV>
 __global__ __launch_bounds__(64 * NWV) void k_route_small(RouterArgs a, PermuteArgs pm) {
-  __shared__ int32_t s_ids[kSmallRoutePairs];
+  __shared__ __align__(16) int32_t s_ids[kSmallRoutePairs];
   __shared__ int32_t s_sorted[kSmallRoutePairs];
+  __shared__ int32_t s_wcount[kSmallRoutePairs / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = a.T * a.K;
+  // positions past the pairs hold a sentinel above every expert id (the rank
+  // loop reads them four at a time)
+  for (int q = n + threadIdx.x; q < ((n + 3) & ~3); q += 64 * NWV) s_ids[q] = 0x7fffffff;
   if constexpr (PL <= 8) {
     if (a.K <= 64) {  // consecutive experts per lane: one wave maximum and one ballot per round
       for (int t = wave; t < a.T; t += NWV) {
@@ -370,19 +375,51 @@ __global__ __launch_bounds__(64 * NWV) void k_route_small(RouterArgs a, PermuteA
                          s_ids + t * a.K);
   }
   __syncthreads();
-  const int n = a.T * a.K, p = threadIdx.x;
+  const int p = threadIdx.x;
   if (p < n) {
     const int e = s_ids[p];
     int rank = 0;
-    for (int q = 0; q < n; ++q) {
-      const int eq = s_ids[q];
-      rank += (eq < e) | ((eq == e) & (q < p));
+    const int4* s4 = reinterpret_cast<const int4*>(s_ids);
+#pragma unroll 4
+    for (int q4 = 0; q4 < (n + 3) >> 2; ++q4) {
+      const int4 v = s4[q4];
+      const int q = 4 * q4;
+      rank += (v.x < e) | ((v.x == e) & (q < p));
+      rank += (v.y < e) | ((v.y == e) & (q + 1 < p));
+      rank += (v.z < e) | ((v.z == e) & (q + 2 < p));
+      rank += (v.w < e) | ((v.w == e) & (q + 3 < p));
     }
     pm.sorted_pairs[rank] = p;
     pm.pair_pos[p] = rank;
+    if (pm.sorted_tok) pm.sorted_tok[rank] = p / a.K;
     s_sorted[rank] = e;
   }
   __syncthreads();
+  if (pm.work) {
+    // the distinct experts in sorted order: position y starts one if it is
+    // the first of its expert; u = the number of starts before y
+    const int y = threadIdx.x;
+    const int e = y < n ? s_sorted[y] : -1;
+    const bool first = y < n && (y == 0 || s_sorted[y - 1] != e);
+    const uint64_t m = __ballot(first);
+    if (y < kSmallRoutePairs && lane == 0) s_wcount[wave] = __popcll(m);
+    __syncthreads();
+    int u = __popcll(m & ((1ull << lane) - 1ull)), U = 0;
+    for (int w = 0; w < kSmallRoutePairs / 64 && w < NWV; ++w) {
+      if (w < wave) u += s_wcount[w];
+      U += s_wcount[w];
+    }
+    int4* work = reinterpret_cast<int4*>(pm.work);
+    if (first) {
+      int lo = y + 1, hi = n;  // end of the run: first position with expert > e
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_sorted[mid] <= e) lo = mid + 1; else hi = mid;
+      }
+      work[u] = make_int4(e, y, lo - y, 0);
+    }
+    if (y >= U && y < n) work[y] = make_int4(-1, 0, 0, 0);
+  }
   for (int e = threadIdx.x; e <= a.E; e += 64 * NWV) {
     int lo = 0, hi = n;  // first rank with expert >= e
     while (lo < hi) {
