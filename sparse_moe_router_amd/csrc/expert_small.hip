@@ -3,13 +3,14 @@
 // (low-bit weights: page 1 "How Strata Makes the Impossible Possible"; SwiGLU
 // expert sub-networks: page 2 "Layer 1"; shared expert: page 5).
 //
-// Block row y is sorted position y (the pairs sorted by expert, as
+// Work row y is sorted position y (the pairs sorted by expert, as
 // moe_permute orders them) and works only if y is its expert's first
 // position; then it owns all of the expert's tokens (sorted positions y ..
-// y + n - 1); the last block row is the shared expert (all T tokens).  The
-// expert's weight rows are loaded once; the tokens' activations are staged in
-// LDS, prepared, chunk by chunk.  Both kernels unpack the codes once for all
-// the tokens.
+// y + n - 1).  With the small-batch routing's work list, row y is instead the
+// y-th distinct expert.  Work row T K is the shared expert (all T tokens),
+// dispatched first.  The expert's weight rows are loaded once; the tokens'
+// activations are staged in LDS, prepared, chunk by chunk.  Both kernels
+// unpack the codes once for all the tokens.
 #include "gemv_one.h"
 
 namespace moe {
@@ -42,6 +43,12 @@ __device__ __forceinline__ bool sb_work(const FfnArgs& a, int ny, int y, int* ex
   return !on_mfma(a, *n);  // the grouped GEMM takes an expert with many tokens
 }
 
+// Block row of the grid -> work row: the shared expert's row (ny), which has
+// every token, goes first in dispatch order, then the experts' rows.
+__device__ __forceinline__ int sb_row(int ny) {
+  return (int)gridDim.y > ny ? ((int)blockIdx.y == 0 ? ny : (int)blockIdx.y - 1) : (int)blockIdx.y;
+}
+
 // token of the expert's jj-th sorted position
 __device__ __forceinline__ int sb_token(const FfnArgs& a, bool shared, int lo, int jj) {
   return shared ? jj : a.sorted_tok ? a.sorted_tok[lo + jj] : a.sorted_pairs[lo + jj] / a.K;
@@ -55,7 +62,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   constexpr int RPW = kSbRpw;
   static_assert(kSbTok == 8, "the first chunk is two tokens per wave");
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int y = blockIdx.y;
+  const int y = sb_row(ny);
   // tokens of the first chunk's positions y + wave and y + wave + 4, read
   // with the expert lookup (clamped in range; used only below the count);
   // with a work list, from the expert's first position once it is known
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(256) void k_down_sb(FfnArgs a, int ny) {
   extern __shared__ __align__(16) uint32_t lds_sb[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int e, lo, n;
-  if (!sb_work(a, ny, blockIdx.y, &e, &lo, &n)) return;
+  if (!sb_work(a, ny, sb_row(ny), &e, &lo, &n)) return;
   const bool shared = e < 0;
   const int G = a.I / kGroup;
   uint4* hq = reinterpret_cast<uint4*>(lds_sb);             // [kSbTok][4][G]
