@@ -27,7 +27,9 @@
  *     MOE_E_DEVICE (a HIP launch error, read from hipGetLastError).  Faults
  *     inside kernels surface at the caller's next synchronisation.
  *   - T == 0 is a valid no-op.  Expert ids handed to moe_permute /
- *     moe_expert_ffn_q must lie in [0, E); others are undefined behaviour.
+ *     moe_expert_ffn_q must lie in [0, E); others are undefined behaviour in
+ *     the release library and MOE_E_ARG in the debug library
+ *     (moe_range_checks).
  *   - Activations: x and the intermediate h are stored in the layer's
  *     activation type (bf16 bits or fp32); router weights, combine weights and
  *     outputs are fp32.  Accumulation is fp32.
@@ -248,6 +250,18 @@ const char *moe_status_str(moe_status s);
 
 /* ABI version, bumped on any change of the structs or signatures above. */
 int32_t moe_abi_version(void);
+
+/* 1 in the debug library (libmoe_debug.so), 0 in the release library.  The
+ * debug library range-checks, on the device, the routing arrays a caller
+ * hands to moe_permute (ids in [0, E)), moe_expert_ffn_q /
+ * moe_expert_gate_up_q / moe_expert_down_q (ids; offsets a non-decreasing
+ * run from 0 to T*K; sorted pairs in [0, T*K)) and moe_combine (pair
+ * positions in [0, T*K)) before any kernel indexes with them, and returns
+ * MOE_E_ARG with nothing else enqueued when one is out of range.  The check
+ * synchronises the stream (the call then returns after the check has run), so
+ * those calls cannot be captured in a HIP graph in the debug library.  (The
+ * ids pick among the E experts, page 2 "Layer 1".) */
+int32_t moe_range_checks(void);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# the same entry points with device range checks of caller-provided routing
+# arrays (select it with use_debug_library)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libmoe_debug.so")
 
 MOE_OK, MOE_E_ARG, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_DEVICE = range(5)
 MOE_Q4_SYM_G32, MOE_Q2_ASYM_G32, MOE_Q3_SYM_G32 = 1, 2, 3
@@ -25,7 +28,8 @@ ACT = {"f32": MOE_ACT_F32, "bf16": MOE_ACT_BF16}
 
 EXPORTS = ("moe_router_topk", "moe_permute", "moe_expert_ffn_q", "moe_expert_gate_up_q", "moe_expert_down_q",
            "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc",
-           "moe_workspace_bytes", "moe_stack_forward", "moe_dequant", "moe_status_str", "moe_abi_version")
+           "moe_workspace_bytes", "moe_stack_forward", "moe_dequant", "moe_status_str", "moe_abi_version",
+           "moe_range_checks")
 
 
 class MoeError(RuntimeError):
@@ -84,8 +88,19 @@ def lib() -> ctypes.CDLL:
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_abi_version.argtypes = []
         L.moe_abi_version.restype = i32
+        L.moe_range_checks.argtypes = []
+        L.moe_range_checks.restype = i32
         _lib = L
     return _lib
+
+
+def use_debug_library(debug: bool = True):
+    """Route every later call to the debug library (or back to the release
+    one).  Layer objects and workspaces stay valid across the switch."""
+    global LIB_PATH, _lib
+    path = DEBUG_LIB_PATH if debug else os.path.join(_HERE, "libmoe.so")
+    if path != LIB_PATH:
+        LIB_PATH, _lib = path, None
 
 
 def _check(fn: str, status: int):
@@ -399,3 +414,7 @@ def moe_dequant(codes, scales, mins, qfmt, rows, cols, out, stream=None):
 
 def moe_abi_version() -> int:
     return int(lib().moe_abi_version())
+
+
+def moe_range_checks() -> int:
+    return int(lib().moe_range_checks())

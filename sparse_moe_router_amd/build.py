@@ -3,7 +3,8 @@
     python -m sparse_moe_router_amd.build
 
 Every source is compiled each time (objects under ``_build/``), then linked
-into ``sparse_moe_router_amd/libmoe.so``.
+into ``sparse_moe_router_amd/libmoe.so`` and, with the entry points' range
+checks compiled in, ``sparse_moe_router_amd/libmoe_debug.so``.
 """
 from __future__ import annotations
 
@@ -17,6 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoe.so")
+OUT_DEBUG = os.path.join(PKG, "libmoe_debug.so")
+DEBUG_SOURCES = ("moe_abi.cpp", "checks.hip")  # the only sources that MOE_RANGE_CHECKS changes
 BUILD = os.path.join(PKG, "_build")
 
 ARCH = "gfx950"
@@ -40,28 +43,40 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, debug: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + (".debug.o" if debug else ".o"))
+    cmd = [hipcc(), *FLAGS, *(["-DMOE_RANGE_CHECKS"] if debug else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Both libraries: the release one and the debug one, whose entry points
+    range-check caller-provided routing arrays (the sources that differ are
+    compiled twice, with MOE_RANGE_CHECKS; the kernels' objects are shared)."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = [(src, False) for src in srcs] + [(src, True) for src in srcs if os.path.basename(src) in DEBUG_SOURCES]
+    with ThreadPoolExecutor(min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    rel = objs[:len(srcs)]
+    dbg_by_src = {os.path.basename(j[0]): o for j, o in zip(jobs[len(srcs):], objs[len(srcs):])}
+    dbg = [dbg_by_src.get(os.path.basename(src), o) for src, o in zip(srcs, rel)]
+    _link(rel, OUT)
+    _link(dbg, OUT_DEBUG)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {OUT_DEBUG}")
     return OUT
 
 

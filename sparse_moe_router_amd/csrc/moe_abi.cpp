@@ -13,7 +13,7 @@ using namespace moe;
 
 constexpr int kMaxDim = 4096;
 constexpr int kMaxExperts = 8192;
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -159,11 +159,34 @@ moe_status layer_forward_impl(const moe_layer& L, const void* x, int32_t T, floa
   return dev(launch_combine(ca, s));
 }
 
+// The debug library checks caller-provided routing arrays on the device
+// before anything indexes with them; the release library takes them as given.
+moe_status range_check(const moe_layer* L, int32_t T, const int32_t* ids, const int32_t* offsets,
+                       const int32_t* sorted, const int32_t* pos, void* stream) {
+#ifdef MOE_RANGE_CHECKS
+  uint32_t err = 0;
+  const RoutingCheck c{ids, offsets, sorted, pos, T, L->top_k, L->n_experts};
+  MOE_TRY(dev(check_routing(c, reinterpret_cast<hipStream_t>(stream), &err)));
+  return err ? MOE_E_ARG : MOE_OK;
+#else
+  (void)L; (void)T; (void)ids; (void)offsets; (void)sorted; (void)pos; (void)stream;
+  return MOE_OK;
+#endif
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t moe_abi_version(void) { return kAbiVersion; }
+
+int32_t moe_range_checks(void) {
+#ifdef MOE_RANGE_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
 
 const char* moe_status_str(moe_status s) {
   switch (s) {
@@ -204,6 +227,7 @@ moe_status moe_permute(const moe_layer* layer, const int32_t* topk_ids, int32_t 
   MOE_TRY(check_tokens(layer, T));
   if (!topk_ids || !expert_offsets || !sorted_pairs || !pair_pos) return MOE_E_ARG;
   MOE_TRY(ws_check(*layer, T, ws, ws_bytes));
+  MOE_TRY(range_check(layer, T, topk_ids, nullptr, nullptr, nullptr, stream));
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const Ws W = ws_layout(*layer, T);
   PermuteArgs pa{topk_ids, expert_offsets, sorted_pairs, pair_pos, at<int32_t>(ws, W.chunk), T, layer->top_k,
@@ -231,6 +255,7 @@ moe_status moe_expert_ffn_q(const moe_layer* layer, const void* x, int32_t T, co
     if (!h) h = at<void>(ws, W.h);
     if (!hs) hs = at<void>(ws, W.hs);
   }
+  MOE_TRY(range_check(layer, T, topk_ids, expert_offsets, sorted_pairs, nullptr, stream));
   const bool shared = layer->shared.n == 1 && shared_out_opt != nullptr;
   const FfnArgs fa = ffn_args(*layer, x, T, topk_ids, expert_offsets, sorted_pairs, h, shared ? hs : nullptr,
                               expert_out, shared ? shared_out_opt : nullptr);
@@ -248,6 +273,7 @@ moe_status moe_expert_gate_up_q(const moe_layer* layer, const void* x, int32_t T
   if (!x || !topk_ids || !expert_offsets || !sorted_pairs || !h || !aligned(x, 16) || !aligned(h, 16))
     return MOE_E_ARG;
   if (shared_h_opt && !aligned(shared_h_opt, 16)) return MOE_E_ARG;
+  MOE_TRY(range_check(layer, T, topk_ids, expert_offsets, sorted_pairs, nullptr, stream));
   const bool shared = layer->shared.n == 1 && shared_h_opt != nullptr;
   const FfnArgs fa = ffn_args(*layer, x, T, topk_ids, expert_offsets, sorted_pairs, h,
                               shared ? shared_h_opt : nullptr, nullptr, nullptr);
@@ -266,6 +292,7 @@ moe_status moe_expert_down_q(const moe_layer* layer, const void* h, const void* 
   if ((shared_h_opt && !aligned(shared_h_opt, 16)) || (shared_out_opt && !aligned(shared_out_opt, 16)))
     return MOE_E_ARG;
   if (shared_out_opt && layer->shared.n == 1 && !shared_h_opt) return MOE_E_ARG;
+  MOE_TRY(range_check(layer, T, topk_ids, expert_offsets, sorted_pairs, nullptr, stream));
   const bool shared = layer->shared.n == 1 && shared_out_opt != nullptr;
   FfnArgs fa = ffn_args(*layer, nullptr, T, topk_ids, expert_offsets, sorted_pairs, const_cast<void*>(h),
                         shared ? const_cast<void*>(shared_h_opt) : nullptr, expert_out,
@@ -282,6 +309,7 @@ moe_status moe_combine(const moe_layer* layer, const float* expert_out, const fl
   if (!expert_out || !pair_pos || !topk_w || !y) return MOE_E_ARG;
   if (!aligned(expert_out, 16) || !aligned(y, 16) || (shared_out_opt && !aligned(shared_out_opt, 16))) return MOE_E_ARG;
   if (x_next_opt && !x_resid) return MOE_E_ARG;
+  MOE_TRY(range_check(layer, T, nullptr, nullptr, nullptr, pair_pos, stream));
   const CombineArgs ca{expert_out, shared_out_opt, pair_pos, topk_w, x_resid, x_next_opt, y,
                        T, layer->hidden, layer->top_k, layer->act};
   return dev(launch_combine(ca, reinterpret_cast<hipStream_t>(stream)));

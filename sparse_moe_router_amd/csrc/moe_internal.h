@@ -69,6 +69,18 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 bool route_small_ok(int T, int K, int E);
 hipError_t launch_route_small(const RouterArgs& a, const PermuteArgs& p, hipStream_t s);
 
+// debug library only: range checks of caller-provided routing arrays (null
+// arrays are skipped); err receives the failed checks' bits, after a
+// synchronisation of s
+struct RoutingCheck {
+  const int32_t* ids;
+  const int32_t* offsets;
+  const int32_t* sorted;
+  const int32_t* pos;
+  int T, K, E;
+};
+hipError_t check_routing(const RoutingCheck& c, hipStream_t s, uint32_t* err);
+
 // ---------------------------------------------------------------- expert FFN
 struct FfnArgs {
   QMat gate, up, down;     // routed, expert 0 base

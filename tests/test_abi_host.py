@@ -34,8 +34,19 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, n), n
 
 
+def test_debug_library_exports_the_same_entry_points_with_range_checks():
+    """libmoe_debug.so: the same symbols; moe_range_checks() tells the two apart."""
+    assert os.path.exists(api.DEBUG_LIB_PATH), "libmoe_debug.so not built"
+    dbg, rel = ctypes.CDLL(api.DEBUG_LIB_PATH), ctypes.CDLL(api.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(dbg, n), n
+    dbg.moe_range_checks.restype = rel.moe_range_checks.restype = ctypes.c_int32
+    assert rel.moe_range_checks() == 0 and dbg.moe_range_checks() == 1
+    assert api.moe_range_checks() == 0  # the binding's default is the release library
+
+
 def test_abi_version_and_status_strings():
-    assert api.moe_abi_version() == 3
+    assert api.moe_abi_version() == 4
     for s in range(5):
         assert api.lib().moe_status_str(s).startswith(b"MOE_")
 
