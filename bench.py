@@ -45,8 +45,8 @@ PEAK_HBM_GBS = 8000.0
 # sources whose fingerprint is stored; reported as null once they change.
 TRAFFIC_SOURCES = ("router.hip", "expert_gemv.hip", "gemv_one.h", "gemv_tile.h", "moe_device.h", "topk.h",
                    "moe_internal.h", "moe_abi.cpp")
-MEASURED_TRAFFIC = {"bytes_per_step": 33959726,
-                    "sources_sha256": "62f7580774a00d99ceae3bf559f49e78c64215079edb84c9b7f7c0c407a3c5b4"}
+MEASURED_TRAFFIC = {"bytes_per_step": 33964462,
+                    "sources_sha256": "6bb2b01ee1c5295a406bd52c733db3bda992e74732bc3eaf0b83fe052a998c05"}
 
 
 def kernel_sources_sha256() -> str:
