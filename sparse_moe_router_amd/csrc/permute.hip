@@ -129,6 +129,63 @@ __global__ __launch_bounds__(64) void k_perm_small(PermuteArgs a) {
   scatter_chunk(a, cnt, 0, n, lane, id_bits(E));
 }
 
+// Up to kSmallMaxPairs pairs and E <= kBlockMaxE experts: one block of
+// kBlockWaves waves, wave w taking the contiguous chunk [w cs, (w+1) cs) of
+// the pairs (cs a multiple of 64).  Phase 1: each wave counts its chunk's ids
+// into its own LDS row; phase 2: thread e turns expert e's counts into
+// running sums over the waves in wave order, a block scan of the totals
+// gives the expert offsets, and row w of expert e becomes the first sorted
+// position of chunk w's pairs of e; phase 3: each wave scatters its chunk in
+// order from its own row (scatter_chunk: a one-wave owner of its LDS row).
+// Chunks in wave order and pairs in order within a chunk keep the sort stable.
+constexpr int kBlockWaves = 16, kBlockMaxE = 512;
+
+__global__ __launch_bounds__(64 * kBlockWaves) void k_perm_block(PermuteArgs a) {
+  extern __shared__ int rows[];  // [kBlockWaves][E]
+  __shared__ int wsum[kBlockWaves];
+  const int E = a.E, n = a.T * a.K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cs = (n + 64 * kBlockWaves - 1) / (64 * kBlockWaves) * 64;
+  const int p0 = min(wave * cs, n), p1 = min(p0 + cs, n);
+  for (int i = tid; i < kBlockWaves * E; i += 64 * kBlockWaves) rows[i] = 0;
+  __syncthreads();
+  int* row = rows + wave * E;
+  // the chunk's ids (at most kSmallMaxPairs / kBlockWaves of them) requested
+  // together before their counts are added
+  constexpr int kRounds = kSmallMaxPairs / kBlockWaves / 64;
+  int ev[kRounds];
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int p = p0 + 64 * i + lane;
+    ev[i] = p < p1 ? a.ids[p] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i)
+    if (ev[i] >= 0) atomicAdd(&row[ev[i]], 1);
+  __syncthreads();
+  int total = 0;
+  if (tid < E) {
+    for (int w = 0; w < kBlockWaves; ++w) {
+      const int c = rows[w * E + tid];
+      rows[w * E + tid] = total;
+      total += c;
+    }
+  }
+  int wtot;
+  const int pre = wave_excl_scan(total, lane, &wtot);
+  if (lane == 0) wsum[wave] = wtot;
+  __syncthreads();
+  int off = pre;
+  for (int w = 0; w < wave; ++w) off += wsum[w];
+  if (tid < E) {
+    a.offsets[tid] = off;
+    for (int w = 0; w < kBlockWaves; ++w) rows[w * E + tid] += off;
+  }
+  if (tid == 0) a.offsets[E] = n;
+  __syncthreads();
+  scatter_chunk(a, row, p0, p1, lane, id_bits(E));
+}
+
 // Multi-block path, phase 1: per-chunk histograms -> chunk_base[c][e].
 __global__ __launch_bounds__(256) void k_perm_hist(PermuteArgs a) {
   extern __shared__ int hist[];
@@ -217,7 +274,10 @@ size_t permute_scratch_ints(int T, int K, int E) {
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   const int n = a.T * a.K;
   if (n <= kSmallMaxPairs) {
-    k_perm_small<<<1, 64, (size_t)a.E * 4, s>>>(a);
+    // a block of 16 waves from 4 rounds of pairs on; one wave below that, or
+    // for more experts than the block's LDS rows hold
+    if (n > 256 && a.E <= kBlockMaxE) k_perm_block<<<1, 64 * kBlockWaves, (size_t)kBlockWaves * a.E * 4, s>>>(a);
+    else k_perm_small<<<1, 64, (size_t)a.E * 4, s>>>(a);
     return hipGetLastError();
   }
   const int chunks = (n + kChunk - 1) / kChunk;

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 // Workgroups are dealt round-robin over the 8 XCDs, so the blocks are
 // numbered such that those of one token tile share an XCD (and its L2 copy of
 // the x tile).  H must be a multiple of 64 (else the fp32 router runs).
-constexpr int kRouterMfmaMinTokens = 128;
+constexpr int kRouterMfmaMinTokens = 64;
 constexpr int kRouterWideTokens = 1024;  // from here on: split over experts
 constexpr int kRChunkK = 64;             // k per chunk
 constexpr int kRInst = 1040;             // LDS bytes per DMA instruction (1 KiB + skew)

@@ -70,12 +70,12 @@ def run_forward(L: api.Layer, x: torch.Tensor, T: int, x_next=False):
 
 # bf16 activations and at least this many tokens: the library evaluates the
 # logits on the matrix cores with each fp32 weight split into three bf16 parts
-ROUTER_MFMA_MIN_TOKENS = 128
+ROUTER_MFMA_MIN_TOKENS = 64
 
 
 def router_parts(spec, T):
     """Parts per weight of the library's logit evaluation for a call of T tokens:
-    3 on the matrix-core path (bf16 x, T >= 128, H a multiple of 64), else 1
+    3 on the matrix-core path (bf16 x, T >= 64, H a multiple of 64), else 1
     (an fp32 dot product)."""
     return 3 if spec.act == synth.ACT_BF16 and T >= ROUTER_MFMA_MIN_TOKENS and spec.hidden % 64 == 0 else 1
 

@@ -716,3 +716,33 @@ def test_bound_calls_match_the_wrappers(family1):
     assert np.array_equal(y0.cpu().numpy(), y1.cpu().numpy())
     assert torch.equal(h0.view(torch.int16), h1.view(torch.int16)) and torch.equal(hs0.view(torch.int16),
                                                                                     hs1.view(torch.int16))
+
+
+# (T, K, E, skew): the permutation kernel each case reaches -- one wave up to
+# 256 pairs, one block of 16 waves up to 4096 pairs at E <= 512, one wave up to
+# 4096 pairs above 512 experts, the three-kernel multi-block path beyond
+PERM_CASES = [(25, 10, 512, 0.0), (26, 10, 512, 1.1), (100, 10, 512, 2.0), (409, 10, 512, 1.1), (128, 32, 100, 0.0),
+              (37, 9, 77, 1.1), (300, 10, 700, 1.1), (500, 10, 512, 1.1)]
+
+
+@pytest.mark.parametrize("case", PERM_CASES, ids=lambda c: "T{}_K{}_E{}_z{}".format(*c))
+def test_permute_paths(case):
+    """moe_permute against the oracle's stable sort, bit for bit, on seeded ids
+    (distinct experts per token, uniform or Zipf-skewed)."""
+    T, K, E, z = case
+    spec = synth.LayerSpec("perm", 64, E, K, 32, T, "q4_sym_g32", "bf16", 0.125, None, family=40 + E + K)
+    ld = synth.gen_layer(spec, routed_ids=[0])
+    L = gu.device_layer(synth.LayerData(spec, 0, ld.router_w, ld.router_b, _repeat_expert(ld.routed, E), ld.shared))
+    rng = np.random.default_rng(T * 1000 + K * 10 + E)
+    p = (1.0 + np.arange(E)) ** -z
+    p /= p.sum()
+    ids = np.stack([rng.choice(E, K, replace=False, p=p) for _ in range(T)]).astype(np.int64)
+    off_w, sp_w, pp_w = mo.permute(ids, E)
+    i32 = dict(dtype=torch.int32, device=gu.DEV)
+    off, sp, pp = torch.empty(E + 1, **i32), torch.empty(T * K, **i32), torch.empty(T * K, **i32)
+    gu.say(f"permute T{T} K{K} E{E} zipf {z}")
+    api.moe_permute(L, torch.from_numpy(ids.astype(np.int32)).to(gu.DEV), T, off, sp, pp, api.workspace(L, T, gu.DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(off.cpu().numpy(), off_w)
+    assert np.array_equal(sp.cpu().numpy(), sp_w)
+    assert np.array_equal(pp.cpu().numpy(), pp_w)
