@@ -706,8 +706,9 @@ static hipError_t fused_gateup_pl(const RouterArgs& r, const PermuteArgs& pm, co
   int lpr_log2, gpl;
   lane_split(a.H, &lpr_log2, &gpl);
   const int rpi = 64 >> lpr_log2;
-  // one token: 2 rows per wave (twice the blocks, each with less to stream after its routing)
-  const int rows_per_block = 4 * (a.T == 1 ? kFusedRpw1 : kRPW) * rpi;
+  // one token (fused_decode_ok): 2 rows per wave (twice the blocks, each with
+  // less to stream after its routing)
+  const int rows_per_block = 4 * kFusedRpw1 * rpi;
   const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, a.T * a.K + (a.n_shared && a.hs ? 1 : 0));
   const int pl = regs_per_lane(a.E);
   if (fused_down1_ok(a.T, a.K, a.E, a.I)) {  // h in slot order for k_fused_down1
@@ -722,23 +723,15 @@ static hipError_t fused_gateup_pl(const RouterArgs& r, const PermuteArgs& pm, co
     }
     return hipGetLastError();
   }
+  // one token with K > 16 or E > 512: the general form (selection per block
+  // row, h in sorted order for the down and combine launches)
   auto go = [&](auto kern) { kern<<<grid, 256, 0, s>>>(r, pm, a, lpr_log2); };
-  if (a.T == 1) {
-    switch (pl) {
-      case 1: go(k_fused_gateup<QF, 1, 1, kFusedRpw1>); break;
-      case 2: go(k_fused_gateup<QF, 1, 2, kFusedRpw1>); break;
-      case 4: go(k_fused_gateup<QF, 1, 4, kFusedRpw1>); break;
-      case 8: go(k_fused_gateup<QF, 1, 8, kFusedRpw1>); break;
-      default: go(k_fused_gateup<QF, 1, 16, kFusedRpw1>); break;
-    }
-  } else {
-    switch (pl) {
-      case 1: go(k_fused_gateup<QF, 4, 1, kRPW>); break;
-      case 2: go(k_fused_gateup<QF, 4, 2, kRPW>); break;
-      case 4: go(k_fused_gateup<QF, 4, 4, kRPW>); break;
-      case 8: go(k_fused_gateup<QF, 4, 8, kRPW>); break;
-      default: go(k_fused_gateup<QF, 4, 16, kRPW>); break;
-    }
+  switch (pl) {
+    case 1: go(k_fused_gateup<QF, 1, 1, kFusedRpw1>); break;
+    case 2: go(k_fused_gateup<QF, 1, 2, kFusedRpw1>); break;
+    case 4: go(k_fused_gateup<QF, 1, 4, kFusedRpw1>); break;
+    case 8: go(k_fused_gateup<QF, 1, 8, kFusedRpw1>); break;
+    default: go(k_fused_gateup<QF, 1, 16, kFusedRpw1>); break;
   }
   return hipGetLastError();
 }
