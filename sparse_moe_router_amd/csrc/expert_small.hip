@@ -213,6 +213,187 @@ __global__ __launch_bounds__(256) void k_down_sb(FfnArgs a, int ny) {
   }
 }
 
+// Layer forward with the small-batch routing's work list: down projection
+// fused with the weighted combine.  A block owns 8 output rows of every
+// distinct expert and of the shared expert, so each token's slots meet in the
+// block and o never leaves it.  All h rows (the T K sorted rows, then the T
+// shared rows) are staged in LDS, prepared, once per block, while the weight
+// rows are in flight.  Wave w takes the work entries w + NW (kFdsEpb b + i)
+// (entry 0: the shared expert, entry u + 1: the u-th distinct expert).  The
+// products have the lane split and the arithmetic of k_down_sb, the combine
+// the order of k_combine (shared first, then slots 0..K-1), so y has the same
+// bits as the step-by-step calls.
+constexpr int kFdsWaves = 16;
+constexpr int kFdsEpb = 2;     // work entries per wave per batch
+constexpr int kFdsRounds = 3;  // staged (row, group) items per thread
+constexpr int kFdsTok = 8;     // tokens of an entry per pass over its groups
+// At most 128 KiB of staged h (T (K + 1) <= 77 rows at I = 768): the block's
+// products run after its h and weights have landed, and past about 80 rows
+// (T = 8, K = 10) they cost what the saved combine launch gains.
+constexpr size_t kFdsMaxLds = 128 * 1024;
+
+// dynamic LDS bytes: prepared h (17 words per row and group), the block's
+// o rows, and the pair -> sorted row map and combine weights
+static size_t fds_lds_bytes(int n, int nh, int G) { return (size_t)nh * (68 * G + 32) + (size_t)n * 8; }
+
+template <int QF, int GPL>
+__global__ __launch_bounds__(64 * kFdsWaves) void k_fused_down_sb(FfnArgs a, CombineArgs c) {
+  extern __shared__ __align__(16) uint32_t lds_fds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool has_shared = a.so != nullptr;
+  const int n = a.T * a.K, nh = n + (has_shared ? a.T : 0), ns = has_shared ? 1 : 0;
+  const int G = a.I / kGroup;
+  uint4* hq = reinterpret_cast<uint4*>(lds_fds);                   // [nh][4][G]
+  float* hc = reinterpret_cast<float*>(lds_fds + nh * 16 * G);     // [nh][G]
+  float* s_o = hc + nh * G;                                          // [nh][8]
+  int32_t* s_pos = reinterpret_cast<int32_t*>(s_o + nh * 8);         // [n]
+  float* s_w = reinterpret_cast<float*>(s_pos + n);                  // [n]
+  const int rbase = blockIdx.x * 8;
+  const int rsub = lane >> 3, sub = lane & 7;
+  // this wave's work entries of a batch; then the combine's inputs and the
+  // h rows are requested (neither waits on the work list; clamped indices
+  // keep the loads out of conditionals), then the entries' weight rows
+  int e[kFdsEpb], lo[kFdsEpb], cnt[kFdsEpb];
+  bool ok[kFdsEpb];
+  RowTile<QF, 1, GPL> tw[kFdsEpb];
+  auto fetch_work = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < kFdsEpb; ++i) {
+      const int j = (kFdsEpb * b + i) * kFdsWaves + wave;
+      const bool sh = has_shared && j == 0;
+      const int4 wk = reinterpret_cast<const int4*>(a.work)[min(max(j - ns, 0), n - 1)];
+      ok[i] = sh || (j - ns < n && wk.x >= 0);
+      e[i] = sh ? -1 : wk.x;
+      lo[i] = sh ? n : wk.y;
+      cnt[i] = sh ? a.T : wk.z;
+    }
+  };
+  auto fetch_weights = [&] {
+#pragma unroll
+    for (int i = 0; i < kFdsEpb; ++i) {
+      const bool sh = e[i] < 0;
+      if (ok[i])
+        tw[i].load(expert_view<QF>(sh ? a.sdown : a.down, sh ? 0 : e[i], a.H, a.I, hot_expert(a, sh, e[i])), rbase,
+                   rsub, kSbLpr, a.H, sub, kSbLpr);
+    }
+  };
+  fetch_work(0);
+  const int p = min((int)threadIdx.x, n - 1);
+  const int32_t pos_v = c.pair_pos[p];
+  const float w_v = c.w[p];
+  XGroup<QF, MOE_ACT_BF16> hg[kFdsRounds];
+#pragma unroll
+  for (int r = 0; r < kFdsRounds; ++r) {
+    const int it = min((int)threadIdx.x + 64 * kFdsWaves * r, nh * G - 1);
+    const int row = it / G, g = it - row * G;
+    const bool sh = row >= n;
+    hg[r].load_raw(sh ? a.hs : a.h, (size_t)(sh ? row - n : row) * a.I + (size_t)g * kGroup);
+  }
+  fetch_weights();
+#pragma unroll
+  for (int r = 0; r < kFdsRounds; ++r) {
+    const int it = (int)threadIdx.x + 64 * kFdsWaves * r;
+    if (it < nh * G) {
+      const int row = it / G, g = it - row * G;
+      hg[r].prep();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        hq[(row * 4 + i) * G + g] = make_uint4(hg[r].p[4 * i], hg[r].p[4 * i + 1], hg[r].p[4 * i + 2], hg[r].p[4 * i + 3]);
+      hc[row * G + g] = hg[r].c;
+    }
+  }
+  if ((int)threadIdx.x < n) {
+    s_pos[threadIdx.x] = pos_v;
+    s_w[threadIdx.x] = w_v;
+  }
+  __syncthreads();
+  for (int b = 0;; ++b) {
+    if (b > 0) {
+      if (!ok[kFdsEpb - 1]) break;  // entries are dense: this wave has no more
+      fetch_work(b);
+      fetch_weights();
+    }
+    if (!ok[0]) break;
+#pragma unroll
+    for (int i = 0; i < kFdsEpb; ++i) {
+      if (!ok[i]) continue;
+      // up to kFdsTok tokens per pass: one group's codes unpacked at a time,
+      // each token's sum still taken over the groups in order
+      for (int j0 = 0; j0 < cnt[i]; j0 += kFdsTok) {
+        const int nj = min(kFdsTok, cnt[i] - j0);
+        float acc[kFdsTok];
+#pragma unroll
+        for (int jj = 0; jj < kFdsTok; ++jj) acc[jj] = 0.f;
+#pragma unroll
+        for (int gi = 0; gi < GPL; ++gi) {
+          uint32_t bw[16];
+          unpack_group<QF>(tw[i].c[0][gi], bw);
+          const int g = min(sub + 8 * gi, G - 1);
+#pragma unroll
+          for (int jj = 0; jj < kFdsTok; ++jj) {
+            if (jj < nj) {
+              const int row = lo[i] + j0 + jj;
+              XGroup<QF, MOE_ACT_BF16> xg;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const uint4 v = hq[(row * 4 + q) * G + g];
+                xg.p[4 * q] = v.x; xg.p[4 * q + 1] = v.y; xg.p[4 * q + 2] = v.z; xg.p[4 * q + 3] = v.w;
+              }
+              xg.c = hc[row * G + g];
+              xg.sx = xg.c;
+              const float v = group_acc_unpacked<QF>(acc[jj], bw, tw[i].s[0][gi], tw[i].m[0][gi], xg);
+              acc[jj] = sub + 8 * gi < G ? v : acc[jj];
+            }
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < kFdsTok; ++jj) {
+          if (jj < nj) {
+            float v = acc[jj];
+            v += dpp_f<kDppXor1>(v);
+            v += dpp_f<kDppXor2>(v);
+            v += dpp_f<kDppHalfMirror>(v);
+            if (sub == 0) s_o[(lo[i] + j0 + jj) * 8 + rsub] = v;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < a.T * 8) {
+    const int t = threadIdx.x >> 3, i = threadIdx.x & 7, r = rbase + i;
+    float acc = has_shared ? s_o[(n + t) * 8 + i] : 0.f;
+    for (int k = 0; k < a.K; ++k) acc = fmaf(s_w[t * a.K + k], s_o[s_pos[t * a.K + k] * 8 + i], acc);
+    if (r < a.H) {
+      const size_t idx = (size_t)t * a.H + r;
+      c.y[idx] = acc;
+      if (c.x_next) store_act<MOE_ACT_BF16>(c.x_next, idx, load_act<MOE_ACT_BF16>(c.x_resid, idx) + acc);
+    }
+  }
+}
+
+bool fused_down_sb_ok(const FfnArgs& a) {
+  // I <= 24 groups: three groups per lane at most (registers of 16 waves)
+  if (!a.work || a.T < 2 || a.act != MOE_ACT_BF16 || a.I % kGroup != 0 || a.I > 24 * kGroup) return false;
+  if (mfma_split(a) != 0) return false;  // every expert on the GEMV kernels
+  const int n = a.T * a.K, nh = n + (a.so ? a.T : 0), G = a.I / kGroup;
+  return n <= 64 * kFdsWaves && a.T * 8 <= 64 * kFdsWaves && (int64_t)nh * G <= 64 * kFdsWaves * kFdsRounds &&
+         fds_lds_bytes(n, nh, G) <= kFdsMaxLds;
+}
+
+hipError_t launch_fused_down_sb(const FfnArgs& a, const CombineArgs& c, hipStream_t s) {
+  const int n = a.T * a.K, nh = n + (a.so ? a.T : 0), G = a.I / kGroup, gpl = (G + 7) / 8;
+  const dim3 grid((a.H + 7) / 8);
+  const size_t lds = fds_lds_bytes(n, nh, G);
+  auto go = [&](auto kern) { kern<<<grid, 64 * kFdsWaves, lds, s>>>(a, c); };
+  by_qfmt(a.qfmt, [&](auto q) {
+    constexpr int QF = decltype(q)::value;
+    if (gpl <= 1) go(k_fused_down_sb<QF, 1>); else if (gpl == 2) go(k_fused_down_sb<QF, 2>);
+    else go(k_fused_down_sb<QF, 3>);
+  });
+  return hipGetLastError();
+}
+
 bool gateup_sb_ok(const FfnArgs& a) {
   return a.T > 1 && a.T * a.K <= kSbMaxPairs && a.act == MOE_ACT_BF16 && a.H <= 64 * kGroup;
 }

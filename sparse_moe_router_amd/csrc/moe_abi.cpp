@@ -155,6 +155,7 @@ moe_status layer_forward_impl(const moe_layer& L, const void* x, int32_t T, floa
     MOE_TRY(dev(launch_permute(pa, s)));
   }
   MOE_TRY(dev(launch_gateup(fa, s)));
+  if (fused_down_sb_ok(fa)) return dev(launch_fused_down_sb(fa, ca, s));  // with the work list only
   MOE_TRY(dev(launch_down(fa, s)));
   return dev(launch_combine(ca, s));
 }

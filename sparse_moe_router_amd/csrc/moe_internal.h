@@ -141,6 +141,11 @@ struct CombineArgs {
   int T, H, K, act;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+// layer forward with the small-batch routing's work list (FfnArgs::work): the
+// down projection fused with the combine, all h rows staged in one block's
+// LDS (T (K + 1) rows up to 128 KiB), no expert on the grouped GEMM
+bool fused_down_sb_ok(const FfnArgs& a);
+hipError_t launch_fused_down_sb(const FfnArgs& a, const CombineArgs& c, hipStream_t s);
 
 // ---------------------------------------------------------------- fused decode path
 // one token: gate/up with the routing (top-K, permutation) recomputed per
