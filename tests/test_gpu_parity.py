@@ -619,6 +619,33 @@ def test_batched_decode_512_experts(T, fmt, family1, family2, family3):
     assert np.array_equal(f["ids"], g["ids"]) and np.array_equal(f["y"], g["y"])
 
 
+@pytest.mark.parametrize("T,shared", [(7, True), (7, False), (8, True), (2, True)])
+def test_small_batch_fused_down_combine(T, shared):
+    """Layer forward of small batches: up to T (K + 1) = 77 staged h rows the
+    down projection and the combine run fused in one kernel whose waves take
+    two work entries per pass (no router bias and 128 experts give more than
+    the 32 entries of one pass, so later passes run too); 88 rows run the two
+    kernels.  Routing, y and x_next against the oracle, and y bitwise against
+    the step-by-step calls."""
+    spec = synth.LayerSpec("fds", 256, 128, 10, 768, T, "q2_asym_g32", "bf16", 0.3, None, family=81,
+                           n_shared=1 if shared else 0)
+    ld = synth.gen_layer(spec)
+    x = synth.gen_x(spec)
+    if shared:
+        g, _ = full_check(ld, x)
+    else:
+        L = gu.device_layer(ld)
+        xd = gu.x_dev(x, spec.act)
+        g = gu.run_steps(L, xd, T, with_shared=False)
+        gu.check_routing(ld, x.values, g)
+        gu.check_permutation(g, spec.n_experts)
+        gu.check_y(ld, x.values, g)
+        f = gu.run_forward(L, xd, T, x_next=True)
+        assert np.array_equal(f["y"], g["y"]), "layer_forward differs from the composed calls"
+        assert np.array_equal(f["x_next"].float().numpy().astype(np.float64), mo.residual_step(x.values, f["y"]))
+    gu.say(f"T={T} shared={shared}: distinct experts {len(np.unique(g['ids']))}")
+
+
 def test_verify_layer():
     spec = synth.SPECS["verify"]
     ld = synth.gen_layer(spec)
