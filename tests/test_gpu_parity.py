@@ -169,6 +169,8 @@ CASES = [
     (96, 64, 1024, 70, 3, "q2_asym_g32", "bf16", True),       # K > 64 slots per token
     (64, 64, 8192, 64, 3, "q4_sym_g32", "bf16", True),        # the most experts the ABI takes, K = 64
     (64, 64, 8192, 64, 1, "q4_sym_g32", "bf16", True),        # the same, one token
+    (4096, 4096, 4, 2, 1, "q4_sym_g32", "bf16", True),        # the largest H and I: one token (GEMV kernels)
+    (4096, 4096, 4, 2, 5, "q3_sym_g32", "bf16", True),        # the largest H and I: a few tokens
 ]
 
 
@@ -196,6 +198,8 @@ MFMA_CASES = [
     (640, 384, 16, 4, 300, "q3_sym_g32", True),     # 3-bit: odd chunk counts, ragged down rows
     (2048, 768, 32, 8, 160, "q3_sym_g32", True),
     (128, 256, 3, 3, 70, "q4_sym_g32", True),       # K = E: every expert takes every token
+    (4096, 4096, 4, 2, 64, "q4_sym_g32", True),     # the largest H and I the ABI takes (32 chunks each way)
+    (4096, 4096, 4, 2, 64, "q2_asym_g32", True),
 ]
 
 
