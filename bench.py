@@ -16,7 +16,8 @@ Prints one JSON line (rank 0, N = 1):
   cpu_baseline the CPU oracle on a bounded sample of the same workload (all
                host cores and one thread)
 plus extra fields: expert-weight GB/s, the directly launched steps (and the
-median of 5 more repetitions), prefill tokens/s and MFMA fraction, the 5-token
+median of 5 more repetitions), the HBM rates a plain device copy and sum reach
+on this GPU, prefill tokens/s and MFMA fraction, the 5-token
 verify batch, a batch sweep T = 8 .. 256 in each weight format, and one decode
 step through the 48-layer 2-bit stack at batch 1 and 8 (expert planes filled
 on the device), each with its distinct experts, algorithmic bytes and fraction
@@ -242,6 +243,10 @@ def main():
         extra["prefill_frac_of_bf16_mfma"] = flops / (pms * 1e-3) / 2.5e15
         log(f"prefill: {pms:.3f} ms/layer, {extra['prefill_tok_s']:.0f} tok/s")
 
+    probe = hbm_probe(dev)
+    extra["hbm_probe"] = probe
+    extra["decode_frac_of_copy_probe"] = achieved / probe["copy_GBps"]
+
     if not args.no_stack:
         extra.update(verify_and_stack(args, dev, q4_layers=layers))
     if not args.no_locality:
@@ -457,6 +462,41 @@ def hot_expert_locality(args, dev):
         del kws
         torch.cuda.empty_cache()
     return out
+
+
+def hbm_probe(dev):
+    """Achievable HBM rates on this GPU with plain library kernels, as context
+    for the 8 TB/s spec: a device-to-device copy of 2 GiB (bytes read plus
+    bytes written over the time) and a sum of 4 GiB of fp32 (bytes read over
+    the time), the median of 5 timed runs of each after two warm runs."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, nbytes):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        r = []
+        for _ in range(5):
+            start.record()
+            fn()
+            end.record()
+            torch.cuda.synchronize()
+            r.append(nbytes / (start.elapsed_time(end) * 1e-3) / 1e9)
+        return float(np.median(r))
+
+    a = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    copy = rate(lambda: b.copy_(a), 2 * a.numel() * 4)
+    del a, b
+    big = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+    read = rate(lambda: big.sum(), big.numel() * 4)
+    del big
+    torch.cuda.empty_cache()
+    log(f"HBM probe: copy {copy:.0f} GB/s (read + write), sum {read:.0f} GB/s (read)")
+    return {"copy_GBps": copy, "sum_read_GBps": read,
+            "how": "torch device copy of 2 GiB (read + written bytes) and torch sum of 4 GiB fp32 (read bytes), "
+                   "median of 5"}
 
 
 def _host_cpu():
