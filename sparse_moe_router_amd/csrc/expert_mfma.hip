@@ -18,14 +18,22 @@
 //   2-bit:  D = sum (1 + u/4) x - sum x      = sum u x / 4,         acc += 4 s D + m sum x
 // Keeping the code in the top mantissa bits keeps the cancelled offset within
 // a few times the signal, so the fp32 sums lose little to the cancellation.
-// The offset sum x is computed once per (token, group) while the activations
-// are staged in LDS.
+// The offset term is formed by one more MFMA per (16-token tile, group), with
+// B = -1.5 (or -1) in every element, in the accumulator layout.
+//
+// Pipeline.  The activations, codes, scales (and minima) of a chunk of 4
+// groups reach LDS by the DMA path (global_load_lds), double buffered, each
+// buffer its own variable, and the reads of the current buffer are issued
+// from asm blocks that wait for themselves: the compiler cannot tell that
+// they do not touch the buffer the next chunk's copies are filling, and would
+// otherwise wait for those copies before every read, so that no copy would
+// run under the products.
 //
 // v_mfma_f32_16x16x32_bf16 lane layout (gfx950): A lane l holds row l % 16,
 // k = 8 (l / 16) .. + 7; B lane l holds column l % 16 at the same k; D lane l
 // holds rows 4 (l / 16) + i, column l % 16.  The codes of one B lane are 8
 // consecutive codes and are unpacked into the pairs (k_j, k_{j+4}); the
-// activations are stored in LDS in that same pair order.
+// activations, copied raw, are put in that same pair order when read.
 #include "gemv_tile.h"
 #include <type_traits>
 
@@ -37,7 +45,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kBM = 64;          // tokens per tile
 constexpr int kXcdTiles = 4;     // tiles per XCD work group
 constexpr int kChunkG = 4;       // groups (of 32 k) per staged chunk
-constexpr int kRowWords = kChunkG * 16 + 4;  // LDS words per token row per chunk (+4 pad: no bank conflicts)
 
 __device__ __forceinline__ f32x4_t mfma16(const uint32_t (&a)[4], const uint32_t (&b)[4], f32x4_t c) {
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
@@ -45,6 +52,52 @@ __device__ __forceinline__ f32x4_t mfma16(const uint32_t (&a)[4], const uint32_t
   const u32x4v bv = {b[0], b[1], b[2], b[3]};
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv),
                                                  c, 0, 0, 0);
+}
+
+// Reads of the buffers the DMA path fills, each batch issued and waited for
+// in one asm block (outputs early-clobber, so no address register doubles as
+// an earlier read's destination).  Read through the compiler, each read would
+// first wait for every copy in flight, the next chunk's included, which are
+// meant to run under this chunk's products.  Addresses are LDS byte offsets.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
+typedef uint32_t frag4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void lds_read4x2(const uint32_t (&a)[4], uint2 (&o)[4]) {
+  u32x2v_t r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b64 %0, %4\n\tds_read_b64 %1, %5\n\tds_read_b64 %2, %6\n\tds_read_b64 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+  o[0] = make_uint2(r0[0], r0[1]); o[1] = make_uint2(r1[0], r1[1]);
+  o[2] = make_uint2(r2[0], r2[1]); o[3] = make_uint2(r3[0], r3[1]);
+}
+// four activation fragments (16 B at fa[i]) and NB code dwords (at ca[i])
+template <int NB>
+__device__ __forceinline__ void grp_read(const uint32_t (&fa)[4], const uint32_t (&ca)[NB], frag4_t (&f)[4],
+                                         uint32_t (&c)[NB]) {
+  if constexpr (NB == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+        "ds_read_b32 %4, %12\n\tds_read_b32 %5, %13\n\tds_read_b32 %6, %14\n\tds_read_b32 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3])
+        : "v"(fa[0]), "v"(fa[1]), "v"(fa[2]), "v"(fa[3]), "v"(ca[0]), "v"(ca[1]), "v"(ca[2]), "v"(ca[3])
+        : "memory");
+  } else {
+    static_assert(NB == 8, "4 or 8 code dwords");
+    asm volatile(
+        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %13\n\tds_read_b128 %2, %14\n\tds_read_b128 %3, %15\n\t"
+        "ds_read_b32 %4, %16\n\tds_read_b32 %5, %17\n\tds_read_b32 %6, %18\n\tds_read_b32 %7, %19\n\t"
+        "ds_read_b32 %8, %20\n\tds_read_b32 %9, %21\n\tds_read_b32 %10, %22\n\tds_read_b32 %11, %23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]),
+          "=&v"(c[4]), "=&v"(c[5]), "=&v"(c[6]), "=&v"(c[7])
+        : "v"(fa[0]), "v"(fa[1]), "v"(fa[2]), "v"(fa[3]), "v"(ca[0]), "v"(ca[1]), "v"(ca[2]), "v"(ca[3]),
+          "v"(ca[4]), "v"(ca[5]), "v"(ca[6]), "v"(ca[7])
+        : "memory");
+  }
 }
 
 // 8 codes of one B lane -> 4 bf16 pairs (k_j, k_{j+4}): 1 + u/16 (4-bit),
@@ -161,12 +214,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int G = kdim / kGroup;  // a multiple of kChunkG (checked by mfma_capable)
   const int nchunks = G / kChunkG;
 
-  __shared__ __align__(16) uint32_t s_a[2][kBM * kRowWords];
-  __shared__ __align__(16) float s_c[2][kChunkG][kBM];  // offset term per (group, token)
-
-  // ---- staging role: thread -> (token row r, group jg of the chunk)
-  const int r = threadIdx.x >> 2, jg = threadIdx.x & 3;
-  const int rr = min(m0 + r, n_rows - 1);  // clamped: rows past the expert's end are dropped at the store
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ln = lane & 15, lc = lane >> 4;
+  // ---- activations: the tile's 64 token rows by the DMA path, in the MFMA
+  // fragment layout: fragment (M tile mt, group j of the chunk) is 1 KiB,
+  // lane l holding row 16 mt + l % 16, elements 8 (l / 16) .. + 7 of the
+  // group (raw bf16; the pair order of the codes is formed when read).  Wave
+  // w copies the fragments of M tile w: its lanes' row (clamped to the
+  // expert's last; such rows are dropped at the store).
+  __shared__ __align__(16) uint8_t s_a0[16 * 1024];
+  __shared__ __align__(16) uint8_t s_a1[16 * 1024];
+  auto sa_of = [&](auto buf_c) -> uint8_t* {
+    if constexpr (decltype(buf_c)::value == 0) return s_a0; else return s_a1;
+  };
+  const int rr = min(m0 + wave * 16 + ln, n_rows - 1);
   const uint16_t* arow;
   if constexpr (NMAT == 2) {
     const int tok = shared ? rr : a.sorted_pairs[lo + rr] / a.K;
@@ -174,33 +235,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   } else {
     arow = reinterpret_cast<const uint16_t*>(shared ? a.hs : a.h) + (size_t)(lo + rr) * kdim;
   }
-  uint4 stage[4];
-  auto load_a = [&](int kc) {
-    const int g = kc * kChunkG + jg;
-    const uint4* src = reinterpret_cast<const uint4*>(arow + (size_t)g * kGroup);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) stage[i] = src[i];
-  };
-  auto store_a = [&](int buf) {
-    uint32_t* dst = &s_a[buf][r * kRowWords + jg * 16];
-    float sx0 = 0.f, sx1 = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {  // chunk of 8: (x0..x7) -> pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7)
-      const uint4 q = stage[c];
-      uint4 p;
-      p.x = (q.x & 0xffffu) | (q.z << 16);
-      p.y = (q.x >> 16) | (q.z & 0xffff0000u);
-      p.z = (q.y & 0xffffu) | (q.w << 16);
-      p.w = (q.y >> 16) | (q.w & 0xffff0000u);
-      *reinterpret_cast<uint4*>(dst + 4 * c) = p;
-      sx0 = dot2_bf16(0x3f803f80u, p.x, sx0);
-      sx1 = dot2_bf16(0x3f803f80u, p.y, sx1);
-      sx0 = dot2_bf16(0x3f803f80u, p.z, sx0);
-      sx1 = dot2_bf16(0x3f803f80u, p.w, sx1);
-    }
-    const float sx = sx0 + sx1;
-    s_c[buf][jg][r] = QF == MOE_Q2_ASYM_G32 ? -sx : -1.5f * sx;
-  };
 
   // ---- weights: the block's 256 row slots (NMAT x 64 WN rows) of codes and
   // scales (and minima) of one chunk, copied global -> LDS by the DMA path
@@ -215,12 +249,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // With these layouts the MFMA lanes' reads below hit 64 distinct banks.
   constexpr int kSlots = NMAT * 64 * WN;  // 256
   constexpr int kCodeChunk = kChunkG * code_bits(QF) * 4;  // code bytes per row per chunk: 64, 48, 32
-  __shared__ __align__(16) uint8_t s_b[2][kSlots * kCodeChunk];
-  __shared__ __align__(16) uint16_t s_s[2][kSlots * kChunkG];
-  __shared__ __align__(16) uint16_t s_m[QF == MOE_Q2_ASYM_G32 ? 2 : 1][QF == MOE_Q2_ASYM_G32 ? kSlots * kChunkG : 8];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ln = lane & 15, lc = lane >> 4;
+  // one variable per buffer (the reads below are issued from asm, so the
+  // compiler does not make them wait for the next chunk's copies)
+  __shared__ __align__(16) uint8_t s_b0[kSlots * kCodeChunk];
+  __shared__ __align__(16) uint8_t s_b1[kSlots * kCodeChunk];
+  __shared__ __align__(16) uint16_t s_s0[kSlots * kChunkG];
+  __shared__ __align__(16) uint16_t s_s1[kSlots * kChunkG];
+  __shared__ __align__(16) uint16_t s_m0[QF == MOE_Q2_ASYM_G32 ? kSlots * kChunkG : 8];
+  __shared__ __align__(16) uint16_t s_m1[QF == MOE_Q2_ASYM_G32 ? kSlots * kChunkG : 8];
+  auto sb_of = [&](auto buf_c) -> uint8_t* {
+    if constexpr (decltype(buf_c)::value == 0) return s_b0; else return s_b1;
+  };
+  auto ss_of = [&](auto buf_c) -> uint16_t* {
+    if constexpr (decltype(buf_c)::value == 0) return s_s0; else return s_s1;
+  };
+  auto sm_of = [&](auto buf_c) -> uint16_t* {
+    if constexpr (decltype(buf_c)::value == 0) return s_m0; else return s_m1;
+  };
   const int eidx = shared ? 0 : expert;
   constexpr int kCodeBytesPerGroup = code_bits(QF) * 4;
   const uint32_t row_bytes = (uint32_t)G * kCodeBytesPerGroup;
@@ -279,14 +324,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int slot = (wave * 2 + i) * 32 + (lane >> 1);
     scale_off[i] = (slot_row(slot) * (uint32_t)G + (uint32_t)(lane & 1) * 2) * 2;  // bytes
   }
-  auto dma_b = [&](int kc, int buf) {
+  auto dma = [&](int kc, auto buf_c, auto mta_c) {
+    constexpr int MTA = decltype(mta_c)::value;
+    if (wave < MTA) {  // this wave's M tile holds tokens: its four fragments of the chunk
+#pragma unroll
+      for (int j = 0; j < kChunkG; ++j)
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const void*>(arow + (size_t)(kc * kChunkG + j) * kGroup + lc * 8),
+            static_cast<void*>(sa_of(buf_c) + (wave * kChunkG + j) * 1024), 16, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < kCodeInst; ++i) {
       const int blk = wave * kCodeInst + i;  // 1 KiB block of the chunk buffer
       const int mi = QF == MOE_Q3_SYM_G32 ? ((blk / 3) * 64) / (64 * WN)
                                           : (blk * (QF == MOE_Q4_SYM_G32 ? 16 : 32)) / (64 * WN);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(cb[mi] + code_off[i] + (uint32_t)kc * kCodeChunk),
-                                       static_cast<void*>(&s_b[buf][blk * 1024]), 16, 0, 0);
+                                       static_cast<void*>(sb_of(buf_c) + blk * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -294,10 +347,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int mi = (blk * 32) / (64 * WN);
       const uint32_t off = scale_off[i] + (uint32_t)kc * (kChunkG * 2);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(reinterpret_cast<const uint8_t*>(sb[mi]) + off),
-                                       static_cast<void*>(&s_s[buf][blk * 128]), 4, 0, 0);
+                                       static_cast<void*>(ss_of(buf_c) + blk * 128), 4, 0, 0);
       if constexpr (QF == MOE_Q2_ASYM_G32)
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(reinterpret_cast<const uint8_t*>(mb[mi]) + off),
-                                         static_cast<void*>(&s_m[buf][blk * 128]), 4, 0, 0);
+                                         static_cast<void*>(sm_of(buf_c) + blk * 128), 4, 0, 0);
     }
   };
 
@@ -317,56 +370,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
       for (int nt = 0; nt < WN; ++nt) acc[mi][mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, auto mta_c) {
+  constexpr float kOff = QF == MOE_Q2_ASYM_G32 ? -1.0f : -1.5f;
+  const uint32_t off2 = (uint32_t)(__float_as_uint(kOff) >> 16) * 0x10001u;  // two bf16 copies (exact)
+  const uint32_t boff[4] = {off2, off2, off2, off2};
+  auto compute = [&](auto buf_c, auto mta_c) {
     constexpr int MTA = decltype(mta_c)::value;  // active 16-row M tiles
+    const uint8_t* sab = sa_of(buf_c);
+    const uint8_t* sbb = sb_of(buf_c);
+    static_assert(NMAT * WN == 4, "four (matrix, N tile) pairs per wave");
     uint2 sc4[NMAT][WN], mn4[NMAT][WN];
+    {
+      uint32_t as[4], am[4];
+      uint2 rs[4], rm[4];
 #pragma unroll
-    for (int mi = 0; mi < NMAT; ++mi)
-#pragma unroll
-      for (int nt = 0; nt < WN; ++nt) {
-        sc4[mi][nt] = *reinterpret_cast<const uint2*>(&s_s[buf][slot_of(mi, nt) * kChunkG]);
-        if constexpr (QF == MOE_Q2_ASYM_G32) mn4[mi][nt] = *reinterpret_cast<const uint2*>(&s_m[buf][slot_of(mi, nt) * kChunkG]);
+      for (int p = 0; p < 4; ++p) {
+        as[p] = lds_addr(ss_of(buf_c) + slot_of(p / WN, p % WN) * kChunkG);
+        am[p] = lds_addr(sm_of(buf_c) + (QF == MOE_Q2_ASYM_G32 ? slot_of(p / WN, p % WN) * kChunkG : 0));
       }
-    struct GroupOps {
+      lds_read4x2(as, rs);
+      if constexpr (QF == MOE_Q2_ASYM_G32) lds_read4x2(am, rm);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        sc4[p / WN][p % WN] = rs[p];
+        mn4[p / WN][p % WN] = QF == MOE_Q2_ASYM_G32 ? rm[p] : make_uint2(0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kChunkG; ++j) {
+      // the group's operands: four activation fragments and the four
+      // (matrix, N tile) pairs' code dwords, in one asm block
+      constexpr int kNB = QF == MOE_Q3_SYM_G32 ? 8 : 4;
+      uint32_t fa[4], ca[kNB];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) fa[mt] = lds_addr(sab + (mt * kChunkG + j) * 1024 + lane * 16);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int slot = slot_of(p / WN, p % WN);
+        if constexpr (QF == MOE_Q4_SYM_G32) {
+          ca[p] = lds_addr(&sbb[(slot >> 4) * 1024 + j * 256 + (slot & 15) * 16 + lc * 4]);
+        } else if constexpr (QF == MOE_Q3_SYM_G32) {
+          // the lane's 8 codes: low-bit bytes 12 j + 2 lc, + 1 and third-bit byte 12 j + 8 + lc of the chunk
+          const uint8_t* base = &sbb[(slot >> 6) * 3072 + (slot & 63) * 16];
+          const int o1 = 12 * j + 2 * lc, o2 = 12 * j + 8 + lc;
+          ca[p] = lds_addr(base + (o1 >> 4) * 1024 + (o1 & 12));      // the dword holding bytes o1, o1 + 1
+          ca[4 + p] = lds_addr(base + (o2 >> 4) * 1024 + (o2 & 12));  // the dword holding byte o2
+        } else {
+          ca[p] = lds_addr(&sbb[(slot >> 5) * 1024 + (j >> 1) * 512 + (slot & 31) * 16 + (j & 1) * 8 + (lc >> 1) * 4]);
+        }
+      }
+      frag4_t fr[4];
+      uint32_t cw[kNB];
+      grp_read<kNB>(fa, ca, fr, cw);
       uint32_t af[4][4];
       f32x4_t cf[4];
       uint32_t bw[NMAT][WN];
-    };
-    auto lds_group = [&](int j, GroupOps& g) {
 #pragma unroll
       for (int mt = 0; mt < MTA; ++mt) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&s_a[buf][(mt * 16 + ln) * kRowWords + j * 16 + lc * 4]);
-        g.af[mt][0] = v.x; g.af[mt][1] = v.y; g.af[mt][2] = v.z; g.af[mt][3] = v.w;
-        g.cf[mt] = *reinterpret_cast<const f32x4_t*>(&s_c[buf][j][mt * 16 + lc * 4]);
+        // (x0..x7) -> pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7), the codes' order
+        af[mt][0] = (fr[mt][0] & 0xffffu) | (fr[mt][2] << 16);
+        af[mt][1] = (fr[mt][0] >> 16) | (fr[mt][2] & 0xffff0000u);
+        af[mt][2] = (fr[mt][1] & 0xffffu) | (fr[mt][3] << 16);
+        af[mt][3] = (fr[mt][1] >> 16) | (fr[mt][3] & 0xffff0000u);
+        cf[mt] = mfma16(af[mt], boff, f32x4_t{0.f, 0.f, 0.f, 0.f});  // the offset term of each token
       }
 #pragma unroll
-      for (int mi = 0; mi < NMAT; ++mi)
-#pragma unroll
-        for (int nt = 0; nt < WN; ++nt) {
-          const int slot = slot_of(mi, nt);
-          if constexpr (QF == MOE_Q4_SYM_G32) {
-            g.bw[mi][nt] = *reinterpret_cast<const uint32_t*>(&s_b[buf][(slot >> 4) * 1024 + j * 256 + (slot & 15) * 16 + lc * 4]);
-          } else if constexpr (QF == MOE_Q3_SYM_G32) {
-            // the lane's 8 codes: low-bit bytes 12 j + 2 lc, + 1 and third-bit byte 12 j + 8 + lc of the chunk
-            const uint8_t* base = &s_b[buf][(slot >> 6) * 3072 + (slot & 63) * 16];
-            const int o1 = 12 * j + 2 * lc, o2 = 12 * j + 8 + lc;
-            const uint32_t lo = *reinterpret_cast<const uint16_t*>(base + (o1 >> 4) * 1024 + (o1 & 15));
-            const uint32_t hi = base[(o2 >> 4) * 1024 + (o2 & 15)];
-            g.bw[mi][nt] = lo | (hi << 16);
-          } else {
-            g.bw[mi][nt] = *reinterpret_cast<const uint16_t*>(
-                &s_b[buf][(slot >> 5) * 1024 + (j >> 1) * 512 + (slot & 31) * 16 + (j & 1) * 8 + lc * 2]);
-          }
+      for (int p = 0; p < 4; ++p) {
+        uint32_t v;
+        if constexpr (QF == MOE_Q4_SYM_G32) {
+          v = cw[p];
+        } else if constexpr (QF == MOE_Q3_SYM_G32) {
+          const int o1 = 12 * j + 2 * lc, o2 = 12 * j + 8 + lc;
+          v = ((cw[p] >> ((o1 & 3) * 8)) & 0xffffu) | (((cw[4 + p] >> ((o2 & 3) * 8)) & 0xffu) << 16);
+        } else {
+          v = (cw[p] >> ((lc & 1) * 16)) & 0xffffu;
         }
-    };
-    GroupOps gops[2];
-    lds_group(0, gops[0]);
-#pragma unroll
-    for (int j = 0; j < kChunkG; ++j) {
-      if (j + 1 < kChunkG) lds_group(j + 1, gops[(j + 1) & 1]);  // next group's operands in flight
-      auto& af = gops[j & 1].af;
-      auto& cf = gops[j & 1].cf;
-      auto& bw = gops[j & 1].bw;
+        bw[p / WN][p % WN] = v;
+      }
       // software pipeline over the NW (matrix, N tile) pairs: the products of
       // pair p are issued before the scaling of pair p - 1
       constexpr int NW = NMAT * WN;
@@ -418,25 +497,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // the DMA writes LDS behind the compiler's back: wait for it (vmcnt) with a
   // memory clobber before the barrier that publishes the chunk
   auto wait_dma = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-  dma_b(0, 0);
-  load_a(0);
-  store_a(0);
-  wait_dma();
-  __syncthreads();
-  // the chunk loop, specialised by the number of 16-row M tiles that hold
-  // tokens of the expert (a partial tile skips the products of its empty ones)
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // one chunk in buffer BUF while the next one is copied into the other
+  auto step = [&](int kc, auto buf_c, auto mta_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    if (kc + 1 < nchunks) dma(kc + 1, std::integral_constant<int, buf ^ 1>{}, mta_c);
+    compute(buf_c, mta_c);
+    wait_dma();
+    __syncthreads();
+  };
+  // the chunk loop, two chunks per pass (buffers 0 and 1), specialised by the
+  // number of 16-row M tiles that hold tokens of the expert (a partial tile
+  // skips the copies and products of its empty ones)
   auto chunks = [&](auto mta_c) {
-    for (int kc = 0; kc < nchunks; ++kc) {
-      const int buf = kc & 1;
-      const bool more = kc + 1 < nchunks;
-      if (more) {
-        dma_b(kc + 1, buf ^ 1);
-        load_a(kc + 1);
-      }
-      compute(buf, mta_c);
-      if (more) store_a(buf ^ 1);
-      wait_dma();
-      __syncthreads();
+    dma(0, B0{}, mta_c);
+    wait_dma();
+    __syncthreads();
+    for (int kc = 0; kc < nchunks; kc += 2) {
+      step(kc, B0{}, mta_c);
+      if (kc + 1 < nchunks) step(kc + 1, B1{}, mta_c);
     }
   };
   const int mt_act = min(4, (n_rows - m0 + 15) / 16);  // uniform
