@@ -426,11 +426,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       uint32_t bw[NMAT][WN];
 #pragma unroll
       for (int mt = 0; mt < MTA; ++mt) {
-        // (x0..x7) -> pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7), the codes' order
-        af[mt][0] = (fr[mt][0] & 0xffffu) | (fr[mt][2] << 16);
-        af[mt][1] = (fr[mt][0] >> 16) | (fr[mt][2] & 0xffff0000u);
-        af[mt][2] = (fr[mt][1] & 0xffffu) | (fr[mt][3] << 16);
-        af[mt][3] = (fr[mt][1] >> 16) | (fr[mt][3] & 0xffff0000u);
+        // (x0..x7) -> pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7), the codes' order;
+        // one byte permute each (bytes 0-3 of the selector's space are the
+        // second operand's, 4-7 the first's)
+        af[mt][0] = __builtin_amdgcn_perm(fr[mt][2], fr[mt][0], 0x05040100u);
+        af[mt][1] = __builtin_amdgcn_perm(fr[mt][2], fr[mt][0], 0x07060302u);
+        af[mt][2] = __builtin_amdgcn_perm(fr[mt][3], fr[mt][1], 0x05040100u);
+        af[mt][3] = __builtin_amdgcn_perm(fr[mt][3], fr[mt][1], 0x07060302u);
         cf[mt] = mfma16(af[mt], boff, f32x4_t{0.f, 0.f, 0.f, 0.f});  // the offset term of each token
       }
 #pragma unroll
