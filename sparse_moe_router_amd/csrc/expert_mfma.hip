@@ -73,29 +73,38 @@ __device__ __forceinline__ void lds_read4x2(const uint32_t (&a)[4], uint2 (&o)[4
   o[0] = make_uint2(r0[0], r0[1]); o[1] = make_uint2(r1[0], r1[1]);
   o[2] = make_uint2(r2[0], r2[1]); o[3] = make_uint2(r3[0], r3[1]);
 }
-// four activation fragments (16 B at fa[i]) and NB code dwords (at ca[i])
-template <int NB>
-__device__ __forceinline__ void grp_read(const uint32_t (&fa)[4], const uint32_t (&ca)[NB], frag4_t (&f)[4],
+// four activation fragments (16 B at abase + AO + 4096 mt, mt = 0..3) and NB
+// code dwords (at cb[i] + BO for the first four, cb[i] + BO2 for the rest);
+// the offsets are the instructions' immediates, so one base register serves
+// every group of a chunk
+template <int NB, int AO, int BO, int BO2>
+__device__ __forceinline__ void grp_read(uint32_t abase, const uint32_t (&cb)[NB], frag4_t (&f)[4],
                                          uint32_t (&c)[NB]) {
   if constexpr (NB == 4) {
     asm volatile(
-        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
-        "ds_read_b32 %4, %12\n\tds_read_b32 %5, %13\n\tds_read_b32 %6, %14\n\tds_read_b32 %7, %15\n\t"
+        "ds_read_b128 %0, %8 offset:%13\n\tds_read_b128 %1, %8 offset:%14\n\t"
+        "ds_read_b128 %2, %8 offset:%15\n\tds_read_b128 %3, %8 offset:%16\n\t"
+        "ds_read_b32 %4, %9 offset:%17\n\tds_read_b32 %5, %10 offset:%17\n\t"
+        "ds_read_b32 %6, %11 offset:%17\n\tds_read_b32 %7, %12 offset:%17\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3])
-        : "v"(fa[0]), "v"(fa[1]), "v"(fa[2]), "v"(fa[3]), "v"(ca[0]), "v"(ca[1]), "v"(ca[2]), "v"(ca[3])
+        : "v"(abase), "v"(cb[0]), "v"(cb[1]), "v"(cb[2]), "v"(cb[3]), "i"(AO), "i"(AO + 4096), "i"(AO + 8192),
+          "i"(AO + 12288), "i"(BO)
         : "memory");
   } else {
     static_assert(NB == 8, "4 or 8 code dwords");
     asm volatile(
-        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %13\n\tds_read_b128 %2, %14\n\tds_read_b128 %3, %15\n\t"
-        "ds_read_b32 %4, %16\n\tds_read_b32 %5, %17\n\tds_read_b32 %6, %18\n\tds_read_b32 %7, %19\n\t"
-        "ds_read_b32 %8, %20\n\tds_read_b32 %9, %21\n\tds_read_b32 %10, %22\n\tds_read_b32 %11, %23\n\t"
+        "ds_read_b128 %0, %12 offset:%21\n\tds_read_b128 %1, %12 offset:%22\n\t"
+        "ds_read_b128 %2, %12 offset:%23\n\tds_read_b128 %3, %12 offset:%24\n\t"
+        "ds_read_b32 %4, %13 offset:%25\n\tds_read_b32 %5, %14 offset:%25\n\t"
+        "ds_read_b32 %6, %15 offset:%25\n\tds_read_b32 %7, %16 offset:%25\n\t"
+        "ds_read_b32 %8, %17 offset:%26\n\tds_read_b32 %9, %18 offset:%26\n\t"
+        "ds_read_b32 %10, %19 offset:%26\n\tds_read_b32 %11, %20 offset:%26\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]),
           "=&v"(c[4]), "=&v"(c[5]), "=&v"(c[6]), "=&v"(c[7])
-        : "v"(fa[0]), "v"(fa[1]), "v"(fa[2]), "v"(fa[3]), "v"(ca[0]), "v"(ca[1]), "v"(ca[2]), "v"(ca[3]),
-          "v"(ca[4]), "v"(ca[5]), "v"(ca[6]), "v"(ca[7])
+        : "v"(abase), "v"(cb[0]), "v"(cb[1]), "v"(cb[2]), "v"(cb[3]), "v"(cb[4]), "v"(cb[5]), "v"(cb[6]),
+          "v"(cb[7]), "i"(AO), "i"(AO + 4096), "i"(AO + 8192), "i"(AO + 12288), "i"(BO), "i"(BO2)
         : "memory");
   }
 }
@@ -105,7 +114,10 @@ __device__ __forceinline__ void grp_read(const uint32_t (&fa)[4], const uint32_t
 // bits in bits 16..23) or 1 + u/4 (2-bit).
 template <int QF>
 __device__ __forceinline__ void unpack_b(uint32_t w, uint32_t (&b)[4]) {
-  asm volatile("" : "+v"(w));  // unpack at the point of use
+  // (no empty asm statement here to pin the unpack: with one, a build whose
+  // group reads used immediate offsets read one MFMA result before the MFMA
+  // had written it; an empty statement emits no instruction, and it sat in
+  // the few slots the compiler counts between that MFMA and the read)
   if constexpr (QF == MOE_Q4_SYM_G32) {  // nibble j -> bits 3..6, nibble j + 4 -> bits 19..22
     b[0] = and_or(w << 3, 0x00780078u, 0x3f803f80u);
     b[1] = and_or(w >> 1, 0x00780078u, 0x3f803f80u);
@@ -246,7 +258,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   //   3-bit codes: per 64 slots 3 KiB laid out [16-byte part q of the
   //                chunk's 48 bytes][slot][16 B]
   //   scales / minima: [slot][4 x fp16]
-  // With these layouts the MFMA lanes' reads below hit 64 distinct banks.
+  // With these layouts the MFMA lanes' reads below hit 64 distinct banks; in
+  // the 4-bit and 2-bit layouts every group of a chunk sits at a fixed
+  // offset from one base address per lane.
   constexpr int kSlots = NMAT * 64 * WN;  // 256
   constexpr int kCodeChunk = kChunkG * code_bits(QF) * 4;  // code bytes per row per chunk: 64, 48, 32
   // one variable per buffer (the reads below are issued from asm, so the
@@ -395,32 +409,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         mn4[p / WN][p % WN] = QF == MOE_Q2_ASYM_G32 ? rm[p] : make_uint2(0u, 0u);
       }
     }
+    // the groups' operands: four activation fragments and the four (matrix,
+    // N tile) pairs' code dwords, one asm block per group; the fragments at
+    // + 1024 j from one base, the 4-bit and 2-bit codes at + kBO from one
+    // base per pair, the 3-bit codes (not at a fixed offset per group in
+    // their layout) from addresses of their own
+    constexpr int kNB = QF == MOE_Q3_SYM_G32 ? 8 : 4;
+    const uint32_t abase = lds_addr(sab + lane * 16);
+    uint32_t cbase[kNB];
 #pragma unroll
-    for (int j = 0; j < kChunkG; ++j) {
-      // the group's operands: four activation fragments and the four
-      // (matrix, N tile) pairs' code dwords, in one asm block
-      constexpr int kNB = QF == MOE_Q3_SYM_G32 ? 8 : 4;
-      uint32_t fa[4], ca[kNB];
+    for (int p = 0; p < 4; ++p) {
+      const int slot = slot_of(p / WN, p % WN);
+      if constexpr (QF == MOE_Q4_SYM_G32) {
+        cbase[p] = lds_addr(&sbb[(slot >> 4) * 1024 + (slot & 15) * 16 + lc * 4]);
+      } else if constexpr (QF == MOE_Q2_ASYM_G32) {
+        cbase[p] = lds_addr(&sbb[(slot >> 5) * 1024 + (slot & 31) * 16 + (lc >> 1) * 4]);
+      }
+    }
+    auto group = [&](auto j_c) {
+      constexpr int j = decltype(j_c)::value;
+      constexpr int kBO = QF == MOE_Q4_SYM_G32 ? j * 256 : QF == MOE_Q2_ASYM_G32 ? (j >> 1) * 512 + (j & 1) * 8 : 0;
+      if constexpr (QF == MOE_Q3_SYM_G32) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) fa[mt] = lds_addr(sab + (mt * kChunkG + j) * 1024 + lane * 16);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int slot = slot_of(p / WN, p % WN);
-        if constexpr (QF == MOE_Q4_SYM_G32) {
-          ca[p] = lds_addr(&sbb[(slot >> 4) * 1024 + j * 256 + (slot & 15) * 16 + lc * 4]);
-        } else if constexpr (QF == MOE_Q3_SYM_G32) {
+        for (int p = 0; p < 4; ++p) {
           // the lane's 8 codes: low-bit bytes 12 j + 2 lc, + 1 and third-bit byte 12 j + 8 + lc of the chunk
+          const int slot = slot_of(p / WN, p % WN);
           const uint8_t* base = &sbb[(slot >> 6) * 3072 + (slot & 63) * 16];
           const int o1 = 12 * j + 2 * lc, o2 = 12 * j + 8 + lc;
-          ca[p] = lds_addr(base + (o1 >> 4) * 1024 + (o1 & 12));      // the dword holding bytes o1, o1 + 1
-          ca[4 + p] = lds_addr(base + (o2 >> 4) * 1024 + (o2 & 12));  // the dword holding byte o2
-        } else {
-          ca[p] = lds_addr(&sbb[(slot >> 5) * 1024 + (j >> 1) * 512 + (slot & 31) * 16 + (j & 1) * 8 + (lc >> 1) * 4]);
+          cbase[p] = lds_addr(base + (o1 >> 4) * 1024 + (o1 & 12));      // the dword holding bytes o1, o1 + 1
+          cbase[4 + p] = lds_addr(base + (o2 >> 4) * 1024 + (o2 & 12));  // the dword holding byte o2
         }
       }
       frag4_t fr[4];
       uint32_t cw[kNB];
-      grp_read<kNB>(fa, ca, fr, cw);
+      grp_read<kNB, j * 1024, kBO, kBO>(abase, cbase, fr, cw);
       uint32_t af[4][4];
       f32x4_t cf[4];
       uint32_t bw[NMAT][WN];
@@ -441,8 +463,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         if constexpr (QF == MOE_Q4_SYM_G32) {
           v = cw[p];
         } else if constexpr (QF == MOE_Q3_SYM_G32) {
-          const int o1 = 12 * j + 2 * lc, o2 = 12 * j + 8 + lc;
-          v = ((cw[p] >> ((o1 & 3) * 8)) & 0xffffu) | (((cw[4 + p] >> ((o2 & 3) * 8)) & 0xffu) << 16);
+          v = ((cw[p] >> ((lc & 1) * 16)) & 0xffffu) | (((cw[4 + p] >> (lc * 8)) & 0xffu) << 16);
         } else {
           v = (cw[p] >> ((lc & 1) * 16)) & 0xffffu;
         }
@@ -493,7 +514,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       // it: left alone, the compiler sinks the scaling past later groups'
       // products and holds every product's result at once)
       __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    group(std::integral_constant<int, 0>{});
+    group(std::integral_constant<int, 1>{});
+    group(std::integral_constant<int, 2>{});
+    group(std::integral_constant<int, 3>{});
+    static_assert(kChunkG == 4, "four groups per chunk");
   };
 
   // the DMA writes LDS behind the compiler's back: wait for it (vmcnt) with a
