@@ -371,6 +371,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // MFMA lanes: this wave's output rows nb + nt * 16 + ln of each matrix
   const int nb = nblk * (64 * WN) + wave * (16 * WN);
   auto slot_of = [&](int mi, int nt) { return mi * 64 * WN + wave * 16 * WN + nt * 16 + ln; };
+  // a group's fp16 scale as fp32, converted by an instruction of its own (left
+  // to the compiler, the conversion folds into a mixed-precision FMA per
+  // product element; the same speed, but the 3-bit kernels then spill more)
+  auto scale_f32 = [](uint2 v, int j) -> float {
+    const uint32_t w = j < 2 ? v.x : v.y;
+    const uint32_t h = (j & 1) ? (w >> 16) : w;
+    float f;
+    asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(h));
+    return f;
+  };
   auto half_of = [](uint2 v, int j) -> float {
     const uint32_t w = j < 2 ? v.x : v.y;
     return f16_to_f32((uint16_t)((j & 1) ? (w >> 16) : (w & 0xffffu)));
@@ -482,7 +492,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           const int mi = p / WN, nt = p % WN;
           uint32_t bf[4];
           unpack_b<QF>(bw[mi][nt], bf);
-          scc = half_of(sc4[mi][nt], j);
+          scc = scale_f32(sc4[mi][nt], j);
           if constexpr (QF == MOE_Q2_ASYM_G32) mnc = half_of(mn4[mi][nt], j) * -0.25f;
 #pragma unroll
           for (int mt = 0; mt < MTA; ++mt) dc[mt] = mfma16(af[mt], bf, cf[mt]);
