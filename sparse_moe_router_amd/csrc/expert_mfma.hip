@@ -115,9 +115,10 @@ __device__ __forceinline__ void grp_read(uint32_t abase, const uint32_t (&cb)[NB
 template <int QF>
 __device__ __forceinline__ void unpack_b(uint32_t w, uint32_t (&b)[4]) {
   // (no empty asm statement here to pin the unpack: with one, a build whose
-  // group reads used immediate offsets read one MFMA result before the MFMA
-  // had written it; an empty statement emits no instruction, and it sat in
-  // the few slots the compiler counts between that MFMA and the read)
+  // group reads used immediate offsets gave wrong values in one accumulator
+  // of the 4-bit gate/up full tiles, and its code had that empty statement
+  // among the few instructions between an MFMA and the first VALU read of its
+  // result; an empty statement emits nothing but may count as a wait state)
   if constexpr (QF == MOE_Q4_SYM_G32) {  // nibble j -> bits 3..6, nibble j + 4 -> bits 19..22
     b[0] = and_or(w << 3, 0x00780078u, 0x3f803f80u);
     b[1] = and_or(w >> 1, 0x00780078u, 0x3f803f80u);
